@@ -1,0 +1,160 @@
+/*
+ * devscan.h -- device-wide prefix sums (scans) and stream compaction for AMD
+ * Instinct MI355X (gfx950), as a plain C ABI.
+ *
+ * Every entry point takes device pointers and an element count, enqueues its
+ * work on `stream` and returns without waiting for it. The caller owns every
+ * pointer it passes and keeps the memory alive until the stream work is done.
+ * The library owns only a small workspace per (device, stream): per-tile
+ * status words, a tile ticket counter and, for the three-pass form, the tile
+ * totals. It grows on demand and is freed by ds_release_workspace().
+ *
+ * Errors. Argument errors are found on the host before any HIP call and
+ * returned at once (DS_ERR_*); launch failures return DS_ERR_HIP. A fault
+ * inside a kernel surfaces, as usual in HIP, at the caller's next
+ * synchronisation of the stream.
+ *
+ * Element types: DS_INT32 / DS_UINT32 / DS_FP32 (4 bytes) and DS_INT64 /
+ * DS_UINT64 (8 bytes), stored contiguously. Integer sums wrap modulo 2^32 or
+ * 2^64 (signed and unsigned give the same bits). fp32 sums are fp32 additions
+ * in an order the library chooses; they meet |y_i - exact_i| <= 1e-5 *
+ * sum_{j<=i} |x_j| at the sizes the tests cover, and may differ in the last
+ * bits from run to run (the look-back can stop at different tiles).
+ * Pointers must be aligned to the element size; 16-byte aligned buffers take
+ * the vectorised path, other aligned buffers a slower scalar one.
+ */
+#ifndef DEVSCAN_H
+#define DEVSCAN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DS_INT32 = 0,
+    DS_UINT32 = 1,
+    DS_FP32 = 2,
+    DS_INT64 = 3,
+    DS_UINT64 = 4
+} ds_dtype;
+
+/* Comparison for compact_if: keep x_i when (x_i OP operand). */
+typedef enum { DS_LT = 0, DS_LE = 1, DS_GT = 2, DS_GE = 3, DS_EQ = 4, DS_NE = 5 } ds_cmp;
+
+/* Device-level algorithm for ds_scan. */
+typedef enum {
+    DS_ALGO_DEFAULT = 0,   /* the single-pass look-back scan */
+    DS_ALGO_LOOKBACK = 1,  /* one launch: tiles publish aggregates / inclusive prefixes and look back */
+    DS_ALGO_THREE_PASS = 2 /* three launches: reduce tiles, scan tile totals, rescan tiles seeded */
+} ds_algo;
+
+typedef enum {
+    DS_OK = 0,
+    DS_ERR_INVALID_VALUE = 1,     /* n < 0, null pointer with n > 0, bad enum value */
+    DS_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not one of ds_dtype */
+    DS_ERR_OVERLAP = 3,           /* input and output overlap without being the same buffer */
+    DS_ERR_MISALIGNED = 4,        /* a pointer not aligned to the element size */
+    DS_ERR_OUT_OF_MEMORY = 5,     /* workspace allocation failed */
+    DS_ERR_HIP = 6,               /* a HIP runtime call or kernel launch failed */
+    DS_ERR_TOO_LARGE = 7          /* n beyond what the entry point supports */
+} ds_status;
+
+/*
+ * Exclusive scan: d_out[0] = 0, d_out[i] = d_in[0] + ... + d_in[i-1].
+ * Defined in "Prefix sum and other parallel patterns" (section "Definitions")
+ * and "Day 31 -- CUDA prefix sum, the Hillis-Steele scan" (section "Two scans,
+ * and which one hands you the total"). Single pass with decoupled look-back
+ * ("Prefix sum and other parallel patterns", section "A device-level scan:
+ * scan then propagate").
+ *   dtype   one of ds_dtype
+ *   d_in    device pointer to n elements (read)
+ *   d_out   device pointer to n elements (written); may equal d_in (in place),
+ *           must not otherwise overlap it
+ *   n       element count, n >= 0; n == 0 enqueues nothing. At most 2^24 - 1
+ *           tiles of 16 KiB: 68,719,472,640 four-byte or 34,359,736,320
+ *           eight-byte elements (DS_ERR_TOO_LARGE beyond)
+ *   stream  HIP stream of the current device (0 = null stream)
+ * Returns DS_OK or a ds_status error.
+ */
+int scan_exclusive(int dtype, const void* d_in, void* d_out, int64_t n, hipStream_t stream);
+
+/*
+ * Inclusive scan: d_out[i] = d_in[0] + ... + d_in[i]. Same sources, arguments
+ * and errors as scan_exclusive.
+ */
+int scan_inclusive(int dtype, const void* d_in, void* d_out, int64_t n, hipStream_t stream);
+
+/*
+ * Either scan with an explicit device-level algorithm: `inclusive` 0 or 1,
+ * `algo` one of ds_algo. DS_ALGO_THREE_PASS is the multi-block scheme of
+ * "Day 32 -- The CUDA scan algorithm: the tree and the three kernels"
+ * (section "One block scans 4,096. Ten million needs three kernels.") in its
+ * reduce-then-scan form: pass 1 only reads (tile totals), pass 2 scans the
+ * totals in one workgroup, pass 3 rescans each tile seeded with its offset.
+ * Other arguments and errors as scan_exclusive.
+ */
+int ds_scan(int dtype, int inclusive, int algo, const void* d_in, void* d_out, int64_t n,
+            hipStream_t stream);
+
+/*
+ * Order-preserving stream compaction: writes, in input order, every d_in[i]
+ * with (d_in[i] CMP operand) to d_out[0 .. k) and k to *d_num_selected (one
+ * int64 in device memory). "Prefix sum and other parallel patterns", section
+ * "Stream compaction" and its first exercise: the write position of a kept
+ * element is the exclusive scan of the keep flags, k = pos[n-1] + flag[n-1].
+ * Flags, positions and the scan of them stay on chip (one launch).
+ *   dtype          one of ds_dtype; comparison in that type's own order
+ *                  (signed, unsigned, IEEE: NaN compares false except DS_NE)
+ *   d_out          room for n elements; may equal d_in, must not otherwise
+ *                  overlap it; elements past k are left untouched
+ *   d_num_selected device pointer to one int64_t (written)
+ *   n              0 <= n < 2^32
+ *   cmp            one of ds_cmp
+ *   operand_bits   the operand's bit pattern in the low 4 or 8 bytes
+ *                  (e.g. the uint32 bits of a float operand)
+ * Returns DS_OK or a ds_status error (DS_ERR_TOO_LARGE for n >= 2^32).
+ */
+int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected, int64_t n,
+               int cmp, uint64_t operand_bits, hipStream_t stream);
+
+/*
+ * Copy of nbytes from d_in to d_out with the same launch shape, 16-byte
+ * accesses and tile size as the 4-byte scan: the practical bandwidth ceiling
+ * the scan is measured against (the "copy, no scan" row of "Day 32 -- The
+ * CUDA scan algorithm", section "Results"). nbytes must be a multiple of 16
+ * and both pointers 16-byte aligned; the buffers must not overlap.
+ */
+int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream);
+
+/*
+ * Waits for `stream` and reports, in *timed_out, whether any look-back wait
+ * on this (device, stream) gave up since the last query (1) or not (0), then
+ * clears the record. A wait gives up only after the spin limit; the outputs of
+ * such a call are not valid. Returns DS_OK or DS_ERR_HIP.
+ */
+int ds_query_timeout(hipStream_t stream, int* timed_out);
+
+/*
+ * Sets the number of polls a look-back wait makes before it gives up
+ * (default 1 << 20; 0 restores the default). Affects later calls in this
+ * process. Small values exist to test the give-up path.
+ */
+int ds_set_spin_limit(uint32_t polls);
+
+/* Human-readable name of a ds_status value (static storage). */
+const char* ds_status_string(int status);
+
+/* Frees every workspace the library holds, after waiting for the device. */
+void ds_release_workspace(void);
+
+/* Library ABI version (1). */
+int ds_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DEVSCAN_H */

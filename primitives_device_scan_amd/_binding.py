@@ -1,0 +1,201 @@
+"""ctypes binding of libdevscan.so (include/devscan.h).
+
+Argument marshalling only: every step of a scan or compaction runs in the HIP
+kernels of the library. torch provides device memory and streams. Importing
+this module fails with ImportError when the library has not been built; there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import struct
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdevscan.so")
+
+# ds_dtype, ds_cmp, ds_algo, ds_status (include/devscan.h)
+DS_INT32, DS_UINT32, DS_FP32, DS_INT64, DS_UINT64 = range(5)
+CMP = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
+ALGO = {"default": 0, "lookback": 1, "three_pass": 2}
+DS_OK = 0
+
+EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_copy", "ds_query_timeout",
+           "ds_set_spin_limit", "ds_status_string", "ds_release_workspace", "ds_version"]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m primitives_device_scan_amd.build` "
+                          "(or __graft_entry__.build()); there is no CPU fallback")
+    L = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    for name in ("scan_exclusive", "scan_inclusive"):
+        getattr(L, name).argtypes = [I, P, P, I64, P]
+        getattr(L, name).restype = I
+    L.ds_scan.argtypes = [I, I, I, P, P, I64, P]
+    L.ds_scan.restype = I
+    L.compact_if.argtypes = [I, P, P, P, I64, I, ctypes.c_uint64, P]
+    L.compact_if.restype = I
+    L.ds_copy.argtypes = [P, P, I64, P]
+    L.ds_copy.restype = I
+    L.ds_query_timeout.argtypes = [P, ctypes.POINTER(I)]
+    L.ds_query_timeout.restype = I
+    L.ds_set_spin_limit.argtypes = [ctypes.c_uint32]
+    L.ds_set_spin_limit.restype = I
+    L.ds_status_string.argtypes = [I]
+    L.ds_status_string.restype = ctypes.c_char_p
+    L.ds_release_workspace.argtypes = []
+    L.ds_release_workspace.restype = None
+    L.ds_version.argtypes = []
+    L.ds_version.restype = I
+    return L
+
+
+lib = load_library()
+
+
+class DevscanError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib.ds_status_string(status).decode()}")
+
+
+def _check(status: int, what: str):
+    if status != DS_OK:
+        raise DevscanError(status, what)
+
+
+_DTYPES = {torch.int32: DS_INT32, torch.float32: DS_FP32, torch.int64: DS_INT64}
+if hasattr(torch, "uint32"):
+    _DTYPES[torch.uint32] = DS_UINT32
+if hasattr(torch, "uint64"):
+    _DTYPES[torch.uint64] = DS_UINT64
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}; one of {list(_DTYPES)}")
+    return _DTYPES[dt]
+
+
+def _stream_handle(x: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensor(x: torch.Tensor, name: str):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def scan(x: torch.Tensor, inclusive: bool, out: torch.Tensor | None = None, *, algo: str = "default",
+         stream=None) -> torch.Tensor:
+    """Exclusive or inclusive scan of the 1-D contiguous GPU tensor x (into out, may be x)."""
+    _check_tensor(x, "x")
+    code = dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    _check_tensor(out, "out")
+    if out.dtype != x.dtype or out.numel() != x.numel() or out.device != x.device:
+        raise ValueError("out must match x in dtype, size and device")
+    with torch.cuda.device(x.device):
+        _check(lib.ds_scan(code, int(bool(inclusive)), ALGO[algo], x.data_ptr(), out.data_ptr(), x.numel(),
+                           _stream_handle(x, stream)), "ds_scan")
+    return out
+
+
+def scan_exclusive(x: torch.Tensor, out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
+    _check_tensor(x, "x")
+    if out is None:
+        out = torch.empty_like(x)
+    _check_tensor(out, "out")
+    if out.dtype != x.dtype or out.numel() != x.numel() or out.device != x.device:
+        raise ValueError("out must match x in dtype, size and device")
+    with torch.cuda.device(x.device):
+        _check(lib.scan_exclusive(dtype_code(x.dtype), x.data_ptr(), out.data_ptr(), x.numel(),
+                                  _stream_handle(x, stream)), "scan_exclusive")
+    return out
+
+
+def scan_inclusive(x: torch.Tensor, out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
+    _check_tensor(x, "x")
+    if out is None:
+        out = torch.empty_like(x)
+    _check_tensor(out, "out")
+    if out.dtype != x.dtype or out.numel() != x.numel() or out.device != x.device:
+        raise ValueError("out must match x in dtype, size and device")
+    with torch.cuda.device(x.device):
+        _check(lib.scan_inclusive(dtype_code(x.dtype), x.data_ptr(), out.data_ptr(), x.numel(),
+                                  _stream_handle(x, stream)), "scan_inclusive")
+    return out
+
+
+def operand_bits(dtype: torch.dtype, value) -> int:
+    """The bit pattern compact_if expects for `value` in `dtype`."""
+    code = dtype_code(dtype)
+    if code == DS_FP32:
+        return struct.unpack("<I", struct.pack("<f", float(value)))[0]
+    if code in (DS_INT32, DS_UINT32):
+        return int(value) & 0xFFFFFFFF
+    return int(value) & 0xFFFFFFFFFFFFFFFF
+
+
+def compact_if(x: torch.Tensor, cmp: str, operand, out: torch.Tensor | None = None,
+               num_selected: torch.Tensor | None = None, *, stream=None):
+    """Order-preserving compaction of x by (x_i cmp operand).
+
+    Returns (out, num_selected): out holds the kept elements in out[:k], and
+    num_selected is a one-element int64 GPU tensor holding k.
+    """
+    _check_tensor(x, "x")
+    code = dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if num_selected is None:
+        num_selected = torch.empty(1, dtype=torch.int64, device=x.device)
+    _check_tensor(out, "out")
+    _check_tensor(num_selected, "num_selected")
+    if out.dtype != x.dtype or out.numel() < x.numel() or out.device != x.device:
+        raise ValueError("out must match x in dtype and device and hold x.numel() elements")
+    if num_selected.dtype != torch.int64 or num_selected.numel() < 1:
+        raise ValueError("num_selected must be an int64 tensor of at least one element")
+    with torch.cuda.device(x.device):
+        _check(lib.compact_if(code, x.data_ptr(), out.data_ptr(), num_selected.data_ptr(), x.numel(), CMP[cmp],
+                              operand_bits(x.dtype, operand), _stream_handle(x, stream)), "compact_if")
+    return out, num_selected
+
+
+def copy(src: torch.Tensor, dst: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """The copy kernel with the scan's access pattern (bandwidth ceiling)."""
+    _check_tensor(src, "src")
+    _check_tensor(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    with torch.cuda.device(src.device):
+        _check(lib.ds_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(src, stream)), "ds_copy")
+    return dst
+
+
+def query_timeout(device=None, stream=None) -> bool:
+    """Waits for the stream; True if a look-back wait gave up since the last query."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        s = torch.cuda.current_stream(dev) if stream is None else stream
+        flag = ctypes.c_int(0)
+        _check(lib.ds_query_timeout(s.cuda_stream if hasattr(s, "cuda_stream") else int(s), ctypes.byref(flag)),
+               "ds_query_timeout")
+    return bool(flag.value)
+
+
+def set_spin_limit(polls: int):
+    _check(lib.ds_set_spin_limit(int(polls)), "ds_set_spin_limit")
+
+
+def release_workspace():
+    lib.ds_release_workspace()

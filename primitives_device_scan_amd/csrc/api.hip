@@ -1,0 +1,264 @@
+// api.hip -- the C ABI of include/devscan.h: argument validation on the host,
+// the per-(device, stream) workspace, and dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "devscan.h"
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace {
+
+using ds::Ctrl;
+using ds::DevWs;
+
+// Workspace layout: [Ctrl][status: 16 B per tile][totals: 8 B per tile].
+struct Workspace {
+    char* base = nullptr;
+    int64_t tile_cap = 0;
+    uint64_t lookback_launches = 0;  // launches that stamped an epoch since the last clear
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+uint32_t g_spin_limit = 1u << 20;
+
+constexpr uint32_t kDefaultSpin = 1u << 20;
+// Epochs are 30 bits: clear the status words well before one comes round again.
+constexpr uint64_t kEpochClearPeriod = 1ull << 29;
+// Largest n: the grid (tiles x 256 work-items) must stay below 2^32 work-items.
+constexpr int64_t kMaxTiles = ((int64_t)1 << 32) / ds::kThreads - 1;
+
+size_t ws_bytes(int64_t tiles) { return sizeof(Ctrl) + (size_t)tiles * 24; }
+
+DevWs view(const Workspace& w)
+{
+    DevWs d;
+    d.ctrl = reinterpret_cast<Ctrl*>(w.base);
+    d.status = reinterpret_cast<uint64_t*>(w.base + sizeof(Ctrl));
+    d.totals = w.base + sizeof(Ctrl) + (size_t)w.tile_cap * 16;
+    return d;
+}
+
+// Returns the workspace of (current device, stream) with room for `tiles`;
+// a new allocation is cleared on the stream before any kernel uses it.
+int get_workspace(hipStream_t stream, int64_t tiles, Workspace** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.tile_cap < tiles) {
+        int64_t cap = w.tile_cap * 2 > tiles ? w.tile_cap * 2 : tiles;
+        if (cap < 1024) cap = 1024;
+        if (w.base) {
+            // The old buffer may still be in use by work queued on the stream.
+            if (hipStreamSynchronize(stream) != hipSuccess) return DS_ERR_HIP;
+            (void)hipFree(w.base);
+            w.base = nullptr;
+            w.tile_cap = 0;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, ws_bytes(cap)) != hipSuccess) {
+            (void)hipGetLastError();
+            return DS_ERR_OUT_OF_MEMORY;
+        }
+        if (hipMemsetAsync(p, 0, ws_bytes(cap), stream) != hipSuccess) {
+            (void)hipFree(p);
+            return DS_ERR_HIP;
+        }
+        w.base = static_cast<char*>(p);
+        w.tile_cap = cap;
+        w.lookback_launches = 0;
+    }
+    if (w.lookback_launches >= kEpochClearPeriod) {
+        if (hipMemsetAsync(w.base + sizeof(Ctrl), 0, (size_t)w.tile_cap * 16, stream) != hipSuccess)
+            return DS_ERR_HIP;
+        w.lookback_launches = 0;
+    }
+    *out = &w;
+    return DS_OK;
+}
+
+bool valid_dtype(int dtype) { return dtype >= DS_INT32 && dtype <= DS_UINT64; }
+
+int elem_bytes(int dtype) { return (dtype == DS_INT64 || dtype == DS_UINT64) ? 8 : 4; }
+
+ds::ElemKind kind_of(int dtype)
+{
+    switch (dtype) {
+    case DS_INT32: return ds::kI32;
+    case DS_UINT32: return ds::kU32;
+    case DS_FP32: return ds::kF32;
+    case DS_INT64: return ds::kI64;
+    default: return ds::kU64;
+    }
+}
+
+// Checks shared by every entry point that reads n elements and writes n.
+int check_io(int dtype, const void* in, const void* out, int64_t n, bool allow_same)
+{
+    if (!valid_dtype(dtype)) return DS_ERR_UNSUPPORTED_DTYPE;
+    if (n < 0) return DS_ERR_INVALID_VALUE;
+    if (n == 0) return DS_OK;
+    if (!in || !out) return DS_ERR_INVALID_VALUE;
+    const int64_t sz = elem_bytes(dtype);
+    const int64_t tiles = (n + ds::tile_elems(sz) - 1) / ds::tile_elems(sz);
+    if (tiles > kMaxTiles) return DS_ERR_TOO_LARGE;
+    if (((uintptr_t)in % sz) || ((uintptr_t)out % sz)) return DS_ERR_MISALIGNED;
+    const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out, len = (uintptr_t)(n * sz);
+    if (a == b) return allow_same ? DS_OK : DS_ERR_OVERLAP;
+    if (a < b + len && b < a + len) return DS_ERR_OVERLAP;
+    return DS_OK;
+}
+
+int scan_impl(int dtype, int inclusive, int algo, const void* in, void* out, int64_t n, hipStream_t stream)
+{
+    if (inclusive != 0 && inclusive != 1) return DS_ERR_INVALID_VALUE;
+    if (algo < DS_ALGO_DEFAULT || algo > DS_ALGO_THREE_PASS) return DS_ERR_INVALID_VALUE;
+    int st = check_io(dtype, in, out, n, true);
+    if (st != DS_OK || n == 0) return st;
+    const int64_t tiles = (n + ds::tile_elems(elem_bytes(dtype)) - 1) / ds::tile_elems(elem_bytes(dtype));
+    std::lock_guard<std::mutex> lock(g_mu);
+    DevWs dws{nullptr, nullptr, nullptr};
+    Workspace* w = nullptr;
+    if (tiles > 1) {
+        st = get_workspace(stream, tiles, &w);
+        if (st != DS_OK) return st;
+        dws = view(*w);
+    }
+    hipError_t e;
+    if (algo == DS_ALGO_THREE_PASS && tiles > 1) {
+        e = ds::launch_three_pass_scan(kind_of(dtype), inclusive != 0, in, out, n, dws, stream);
+    } else {
+        e = ds::launch_lookback_scan(kind_of(dtype), inclusive != 0, in, out, n, dws, g_spin_limit, stream);
+        if (w && e == hipSuccess) ++w->lookback_launches;
+    }
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int scan_exclusive(int dtype, const void* d_in, void* d_out, int64_t n, hipStream_t stream)
+{
+    return scan_impl(dtype, 0, DS_ALGO_DEFAULT, d_in, d_out, n, stream);
+}
+
+int scan_inclusive(int dtype, const void* d_in, void* d_out, int64_t n, hipStream_t stream)
+{
+    return scan_impl(dtype, 1, DS_ALGO_DEFAULT, d_in, d_out, n, stream);
+}
+
+int ds_scan(int dtype, int inclusive, int algo, const void* d_in, void* d_out, int64_t n, hipStream_t stream)
+{
+    return scan_impl(dtype, inclusive, algo, d_in, d_out, n, stream);
+}
+
+int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected, int64_t n, int cmp,
+               uint64_t operand_bits, hipStream_t stream)
+{
+    if (!valid_dtype(dtype)) return DS_ERR_UNSUPPORTED_DTYPE;
+    if (cmp < DS_LT || cmp > DS_NE) return DS_ERR_INVALID_VALUE;
+    if (!d_num_selected || n < 0) return DS_ERR_INVALID_VALUE;
+    if (((uintptr_t)d_num_selected) % 8) return DS_ERR_MISALIGNED;
+    if (n >= ((int64_t)1 << 32)) return DS_ERR_TOO_LARGE;
+    int st = check_io(dtype, d_in, d_out, n, true);
+    if (st != DS_OK) return st;
+    if (n == 0) {
+        // Nothing to scan: the count is 0, written with a copy from the host.
+        static const int64_t zero = 0;
+        return hipMemcpyAsync(d_num_selected, &zero, sizeof(zero), hipMemcpyHostToDevice, stream) == hipSuccess
+                   ? DS_OK
+                   : DS_ERR_HIP;
+    }
+    const int64_t tiles = (n + ds::tile_elems(elem_bytes(dtype)) - 1) / ds::tile_elems(elem_bytes(dtype));
+    std::lock_guard<std::mutex> lock(g_mu);
+    DevWs dws{nullptr, nullptr, nullptr};
+    Workspace* w = nullptr;
+    if (tiles > 1) {
+        st = get_workspace(stream, tiles, &w);
+        if (st != DS_OK) return st;
+        dws = view(*w);
+    }
+    const hipError_t e = ds::launch_compact(kind_of(dtype), d_in, d_out, d_num_selected, n, cmp, operand_bits, dws,
+                                            g_spin_limit, stream);
+    if (w && e == hipSuccess) ++w->lookback_launches;
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream)
+{
+    if (nbytes < 0 || (nbytes % 16)) return DS_ERR_INVALID_VALUE;
+    if (nbytes == 0) return DS_OK;
+    if (!d_in || !d_out) return DS_ERR_INVALID_VALUE;
+    if (((uintptr_t)d_in % 16) || ((uintptr_t)d_out % 16)) return DS_ERR_MISALIGNED;
+    const uintptr_t a = (uintptr_t)d_in, b = (uintptr_t)d_out, len = (uintptr_t)nbytes;
+    if (a < b + len && b < a + len) return DS_ERR_OVERLAP;
+    if (nbytes / ds::kTileBytes >= kMaxTiles) return DS_ERR_TOO_LARGE;
+    return ds::launch_copy(d_in, d_out, nbytes, stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+int ds_query_timeout(hipStream_t stream, int* timed_out)
+{
+    if (!timed_out) return DS_ERR_INVALID_VALUE;
+    *timed_out = 0;
+    if (hipStreamSynchronize(stream) != hipSuccess) return DS_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end() || !it->second.base) return DS_OK;
+    Ctrl* c = reinterpret_cast<Ctrl*>(it->second.base);
+    uint32_t flag = 0;
+    if (hipMemcpy(&flag, &c->timeout, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return DS_ERR_HIP;
+    if (flag) {
+        // Nothing runs on the stream now: clear the record and restart the
+        // ticket counter, which a give-up leaves right but a corrupted counter
+        // (the other reason the flag is set) would not.
+        const uint32_t zero = 0;
+        if (hipMemcpy(&c->timeout, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(&c->ticket, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+            return DS_ERR_HIP;
+    }
+    *timed_out = flag ? 1 : 0;
+    return DS_OK;
+}
+
+int ds_set_spin_limit(uint32_t polls)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_spin_limit = polls ? polls : kDefaultSpin;
+    return DS_OK;
+}
+
+const char* ds_status_string(int status)
+{
+    switch (status) {
+    case DS_OK: return "DS_OK";
+    case DS_ERR_INVALID_VALUE: return "DS_ERR_INVALID_VALUE: bad argument (n < 0, null pointer, bad enum)";
+    case DS_ERR_UNSUPPORTED_DTYPE: return "DS_ERR_UNSUPPORTED_DTYPE";
+    case DS_ERR_OVERLAP: return "DS_ERR_OVERLAP: input and output partially overlap";
+    case DS_ERR_MISALIGNED: return "DS_ERR_MISALIGNED: pointer not aligned to the element size";
+    case DS_ERR_OUT_OF_MEMORY: return "DS_ERR_OUT_OF_MEMORY: workspace allocation failed";
+    case DS_ERR_HIP: return "DS_ERR_HIP: a HIP call or kernel launch failed";
+    case DS_ERR_TOO_LARGE: return "DS_ERR_TOO_LARGE: n beyond the entry point's limit";
+    default: return "unknown ds_status";
+    }
+}
+
+void ds_release_workspace(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_ws.empty()) (void)hipDeviceSynchronize();
+    for (auto& kv : g_ws)
+        if (kv.second.base) (void)hipFree(kv.second.base);
+    g_ws.clear();
+}
+
+int ds_version(void) { return 1; }
+
+}  // extern "C"

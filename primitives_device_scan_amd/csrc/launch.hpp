@@ -1,0 +1,35 @@
+// launch.hpp -- host-side launchers of the scan kernels (kernels.hip), called
+// by the C ABI (api.cpp) after it has validated the arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds {
+
+struct Ctrl;
+
+// Device memory of one workspace.
+struct DevWs {
+    Ctrl* ctrl;          // control words (ticket, epoch, timeout)
+    uint64_t* status;    // 2 x 64-bit words per tile (look-back status)
+    void* totals;        // 8 bytes per tile (three-pass tile totals)
+};
+
+enum ElemKind { kU32 = 0, kF32 = 1, kU64 = 2, kI32 = 3, kI64 = 4 };
+
+int64_t tile_elems(int elem_bytes);
+
+hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
+                                const DevWs& ws, uint32_t spin_limit, hipStream_t stream);
+
+hipError_t launch_three_pass_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
+                                  const DevWs& ws, hipStream_t stream);
+
+hipError_t launch_compact(ElemKind kind, const void* in, void* out, int64_t* num_selected, int64_t n,
+                          int cmp, uint64_t operand_bits, const DevWs& ws, uint32_t spin_limit,
+                          hipStream_t stream);
+
+hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t stream);
+
+}  // namespace ds

@@ -1,0 +1,347 @@
+// tile.hpp -- gfx950 device building blocks of the scan: per-thread register
+// scans over 16-byte vectors, 64-lane wavefront scans on DPP, the workgroup
+// scan of wave totals in LDS, and the per-tile status words of the
+// single-pass look-back.
+//
+// Tile layout (all kernels): a workgroup of 256 threads (4 waves of 64) owns
+// one tile of 16 KiB -- 4,096 four-byte or 2,048 eight-byte elements. Wave w
+// owns the w-th quarter of the tile; in it, lane l holds the 16-byte vectors
+// k*64 + l for k = 0..3. Every load and store instruction of a wave therefore
+// covers 1 KiB of contiguous memory, and the scan order inside the wave is
+// (vector k, lane, element in vector), which is the memory order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kVecsPerThread = 4;
+constexpr int kVecBytes = 16;
+constexpr int kTileBytes = kThreads * kVecsPerThread * kVecBytes;  // 16 KiB
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte access
+
+template <typename T>
+struct Shape {
+    static constexpr int kPerVec = kVecBytes / (int)sizeof(T);   // elements per 16-byte vector
+    static constexpr int kItems = kPerVec * kVecsPerThread;      // elements per thread
+    static constexpr int kWaveElems = kWave * kItems;            // elements per wave
+    static constexpr int kTile = kThreads * kItems;              // elements per tile
+};
+
+// Launch-wide control words, kept in the workspace.
+struct Ctrl {
+    uint32_t ticket;    // next tile ticket; the last tile of a launch resets it to 0
+    uint32_t epoch;     // 30-bit launch number stamped into status words
+    uint32_t timeout;   // set to 1 when a look-back wait gave up
+    uint32_t pad[61];
+};
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane moves. update_dpp with old = 0: lanes whose source lane lies
+// outside the pattern, or whose row is masked off, read 0 -- the identity of
+// addition for every type here (+0.0 for floats).
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWS = 0xf, typename T>
+__device__ __forceinline__ T dpp(T x)
+{
+    if constexpr (sizeof(T) == 4) {
+        const int u = __builtin_bit_cast(int, x);
+        return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, u, CTRL, ROWS, 0xf, false));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xf, false);
+        const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xf, false);
+        return __builtin_bit_cast(T, (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T readlane(T x, int src)
+{
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+        return __builtin_bit_cast(T, (uint64_t)lo | ((uint64_t)hi << 32));
+    }
+}
+
+// Inclusive scan over the 64 lanes of a wave: Hillis-Steele steps 1, 2, 4, 8
+// inside each row of 16 lanes (row_shr), then lane 15 of rows 0 and 2 is added
+// into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31). Six dependent adds; every lane must be active.
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T x)
+{
+    x = x + dpp<0x111>(x);       // row_shr:1
+    x = x + dpp<0x112>(x);       // row_shr:2
+    x = x + dpp<0x114>(x);       // row_shr:4
+    x = x + dpp<0x118>(x);       // row_shr:8
+    x = x + dpp<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+    x = x + dpp<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
+// Lane l receives lane l-1's value, lane 0 receives 0 (wave_shr:1): turns an
+// inclusive scan into an exclusive one without a subtraction.
+template <typename T>
+__device__ __forceinline__ T wave_shift_right1(T x) { return dpp<0x138>(x); }
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) { return readlane(wave_inclusive_scan(x), kWave - 1); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// ---------------------------------------------------------------------------
+// Tile loads and stores.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ int64_t elem_index(int64_t seg, int k, int j, int lane)
+{
+    return seg + (int64_t)(k * kWave + lane) * Shape<T>::kPerVec + j;
+}
+
+// Whole wave segment in range and 16-byte aligned: one 16-byte load per vector.
+template <typename T>
+__device__ __forceinline__ void load_vec(const T* __restrict__ in, int64_t seg, int lane,
+                                         T (&e)[Shape<T>::kItems])
+{
+    const u32x4* p = reinterpret_cast<const u32x4*>(in + seg) + lane;
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k) {
+        const u32x4 r = __builtin_nontemporal_load(p + k * kWave);
+        __builtin_memcpy(&e[k * Shape<T>::kPerVec], &r, kVecBytes);
+    }
+}
+
+// Element-wise, guarded: elements at or past n read as `fill`.
+template <typename T>
+__device__ __forceinline__ void load_scalar(const T* __restrict__ in, int64_t seg, int64_t n, int lane,
+                                            T (&e)[Shape<T>::kItems], T fill)
+{
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k)
+#pragma unroll
+        for (int j = 0; j < Shape<T>::kPerVec; ++j) {
+            const int64_t i = elem_index<T>(seg, k, j, lane);
+            e[k * Shape<T>::kPerVec + j] = i < n ? in[i] : fill;
+        }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_vec(T* __restrict__ out, int64_t seg, int lane,
+                                          const T (&e)[Shape<T>::kItems])
+{
+    u32x4* p = reinterpret_cast<u32x4*>(out + seg) + lane;
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k) {
+        u32x4 r;
+        __builtin_memcpy(&r, &e[k * Shape<T>::kPerVec], kVecBytes);
+        __builtin_nontemporal_store(r, p + k * kWave);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_scalar(T* __restrict__ out, int64_t seg, int64_t n, int lane,
+                                             const T (&e)[Shape<T>::kItems])
+{
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k)
+#pragma unroll
+        for (int j = 0; j < Shape<T>::kPerVec; ++j) {
+            const int64_t i = elem_index<T>(seg, k, j, lane);
+            if (i < n) out[i] = e[k * Shape<T>::kPerVec + j];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Scan of one tile held in registers, up to the tile's own offsets.
+//
+// V is the number of elements per 16-byte vector of the data (4 or 2); T is
+// the type being summed (the data, or 32-bit keep counts in compaction).
+// In: e = the thread's values. Out: e = inclusive prefix inside each vector
+// (the serial scan of the thread's chunk), off[k] = sum of everything in the
+// wave before vector k of this lane, wave_excl = sum of the waves before this
+// one, return value = the tile aggregate. s_wave is kWaves values of LDS.
+// Contains one workgroup barrier.
+// ---------------------------------------------------------------------------
+template <typename T, int V>
+__device__ __forceinline__ T tile_local_scan(T (&e)[V * kVecsPerThread], T (&off)[kVecsPerThread],
+                                             T& wave_excl, T* s_wave)
+{
+    const int lane = lane_id();
+    const int wave = (int)(threadIdx.x / kWave);
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k)
+#pragma unroll
+        for (int j = 1; j < V; ++j)
+            e[k * V + j] = e[k * V + j] + e[k * V + j - 1];
+
+    T incl[kVecsPerThread];
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k)
+        incl[k] = wave_inclusive_scan(e[k * V + V - 1]);
+
+    T run = T(0);
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k) {
+        off[k] = run + wave_shift_right1(incl[k]);
+        run = run + readlane(incl[k], kWave - 1);
+    }
+    if (lane == 0) s_wave[wave] = run;
+    __syncthreads();
+    T agg = T(0), before = T(0);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const T v = s_wave[w];
+        if (w < wave) before = before + v;
+        agg = agg + v;
+    }
+    wave_excl = before;
+    return agg;
+}
+
+// Final values from the local scan and the tile's exclusive prefix.
+template <typename T, int V, bool INCLUSIVE>
+__device__ __forceinline__ void tile_finish(T (&e)[V * kVecsPerThread], const T (&off)[kVecsPerThread],
+                                            T wave_excl, T prefix)
+{
+    const T head = prefix + wave_excl;
+#pragma unroll
+    for (int k = 0; k < kVecsPerThread; ++k) {
+        const T base = head + off[k];
+        if constexpr (INCLUSIVE) {
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                e[k * V + j] = base + e[k * V + j];
+        } else {
+#pragma unroll
+            for (int j = V - 1; j > 0; --j)
+                e[k * V + j] = base + e[k * V + j - 1];
+            e[k * V] = base;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Status words of the single-pass look-back.
+//
+// A 4-byte value travels in one 64-bit word: bits 0-31 the value, bits 32-33
+// the flag (0 nothing yet, 1 aggregate of this tile only, 2 inclusive prefix
+// through this tile), bits 34-63 the launch epoch. A word whose epoch is not
+// the current launch's reads as "nothing yet", so the array never needs
+// clearing between launches. An 8-byte value travels in two such words (low
+// and high halves, same flag and epoch); a reader accepts the pair only when
+// both words carry the same flag and the current epoch, which rules out a
+// torn read because each flag is written once per launch.
+//
+// Words are written and read with relaxed device-scope atomics: coherent
+// across the XCDs' separate L2 caches, with no cache writeback or invalidate.
+// Each word carries its own value, so no ordering with other memory is needed.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kFlagNone = 0, kFlagAggregate = 1, kFlagPrefix = 2;
+constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
+
+__device__ __forceinline__ void status_store(uint64_t* p, uint64_t w)
+{
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t status_load(uint64_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t status_word(uint32_t epoch, uint32_t flag, uint32_t bits)
+{
+    return ((uint64_t)((epoch << 2) | flag) << 32) | bits;
+}
+
+template <typename T>
+struct StatusCodec {
+    static constexpr int kWords = sizeof(T) / 4;  // 64-bit words per tile
+
+    static __device__ __forceinline__ void publish(uint64_t* status, int64_t tile, uint32_t epoch,
+                                                   uint32_t flag, T v)
+    {
+        if constexpr (sizeof(T) == 4) {
+            status_store(status + tile, status_word(epoch, flag, __builtin_bit_cast(uint32_t, v)));
+        } else {
+            const uint64_t u = __builtin_bit_cast(uint64_t, v);
+            status_store(status + 2 * tile, status_word(epoch, flag, (uint32_t)u));
+            status_store(status + 2 * tile + 1, status_word(epoch, flag, (uint32_t)(u >> 32)));
+        }
+    }
+
+    // Reads tile `idx`'s status; returns its flag (kFlagNone when stale or torn).
+    static __device__ __forceinline__ uint32_t read(uint64_t* status, int64_t idx, uint32_t epoch, T& v)
+    {
+        if constexpr (sizeof(T) == 4) {
+            const uint64_t w = status_load(status + idx);
+            const uint32_t hi = (uint32_t)(w >> 32);
+            v = __builtin_bit_cast(T, (uint32_t)w);
+            return (hi >> 2) == epoch ? (hi & 3u) : kFlagNone;
+        } else {
+            const uint64_t w0 = status_load(status + 2 * idx);
+            const uint64_t w1 = status_load(status + 2 * idx + 1);
+            const uint32_t h0 = (uint32_t)(w0 >> 32), h1 = (uint32_t)(w1 >> 32);
+            v = __builtin_bit_cast(T, (uint64_t)(uint32_t)w0 | (w1 << 32));
+            return (h0 == h1 && (h0 >> 2) == epoch) ? (h0 & 3u) : kFlagNone;
+        }
+    }
+};
+
+// Decoupled look-back, run by one whole wave for tile `tile` (> 0) after the
+// tile's aggregate is known. Publishes the aggregate, then reads the status of
+// the 64 preceding tiles at once (lane l reads tile - 1 - l), waits while any
+// tile up to the nearest inclusive prefix has published nothing, adds the
+// aggregates and that prefix, and moves 64 tiles further back when the window
+// holds no prefix. Publishes this tile's inclusive prefix and returns the
+// exclusive one. A wait that exceeds `spin_limit` polls gives up: the missing
+// values count as 0 and `timeout` is set, so every wave still finishes.
+template <typename T>
+__device__ T lookback(uint64_t* status, int64_t tile, uint32_t epoch, T agg, uint32_t spin_limit,
+                      uint32_t* timeout)
+{
+    using C = StatusCodec<T>;
+    const int lane = lane_id();
+    if (lane == 0) C::publish(status, tile, epoch, kFlagAggregate, agg);
+    T acc = T(0);
+    int64_t base = tile - 1;
+    uint32_t polls = 0;
+    bool gave_up = false;
+    for (;;) {
+        const int64_t idx = base - lane;
+        T v = T(0);
+        uint32_t flag = kFlagPrefix;  // before tile 0: an inclusive prefix of 0
+        if (idx >= 0) flag = C::read(status, idx, epoch, v);
+        const uint64_t pm = ballot(flag == kFlagPrefix);
+        const uint64_t xm = ballot(flag == kFlagNone);
+        const uint64_t upto = pm ? (pm ^ (pm - 1)) : ~0ull;  // lanes up to the first prefix
+        if ((xm & upto) && !gave_up) {
+            if (++polls < spin_limit) {
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+            }
+            gave_up = true;
+            if (lane == 0) __hip_atomic_store(timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const bool take = ((upto >> lane) & 1ull) && flag != kFlagNone;
+        acc = acc + wave_sum(take ? v : T(0));
+        if (pm) break;
+        base -= kWave;
+    }
+    if (lane == 0) C::publish(status, tile, epoch, kFlagPrefix, acc + agg);
+    return acc;
+}
+
+}  // namespace ds

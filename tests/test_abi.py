@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every function include/*.h declares, and
+rejects bad arguments on the host before any HIP call (CPU only: none of
+these calls reaches a kernel launch)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "primitives_device_scan_amd", "libdevscan.so")
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.append(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import primitives_device_scan_amd.build as b
+        b.build()
+    from primitives_device_scan_amd import _binding
+    return _binding.load_library(LIB)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("scan_exclusive", "scan_inclusive", "compact_if", "ds_scan", "ds_copy"):
+        assert want in names, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in include/ but not exported"
+    from primitives_device_scan_amd import _binding
+    assert sorted(_binding.EXPORTS) == sorted(declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ds_version() == 1
+    for s in range(8):
+        assert lib.ds_status_string(s).startswith(b"DS_")
+    assert b"unknown" in lib.ds_status_string(99)
+
+
+# Fake, never-dereferenced addresses: validation must reject these on the host.
+A = 0x7F0000000000
+B = 0x7F0000100000
+
+
+@pytest.mark.parametrize("fn", ["scan_exclusive", "scan_inclusive"])
+def test_scan_validation(lib, fn):
+    f = getattr(lib, fn)
+    assert f(7, A, B, 10, None) == 2            # DS_ERR_UNSUPPORTED_DTYPE
+    assert f(-1, A, B, 10, None) == 2
+    assert f(0, A, B, -1, None) == 1            # n < 0
+    assert f(0, None, B, 10, None) == 1         # null with n > 0
+    assert f(0, A, None, 10, None) == 1
+    assert f(0, None, None, 0, None) == 0       # n == 0: nothing to do, no launch
+    assert f(0, A, A + 4, 10, None) == 3        # partial overlap
+    assert f(0, A + 4, A, 10, None) == 3
+    assert f(0, A + 2, B, 10, None) == 4        # misaligned for int32
+    assert f(3, A + 4, B, 10, None) == 4        # misaligned for int64
+    assert f(0, A, B, 1 << 40, None) == 7       # beyond the grid limit
+
+
+def test_ds_scan_validation(lib):
+    assert lib.ds_scan(0, 2, 0, A, B, 10, None) == 1   # inclusive not 0/1
+    assert lib.ds_scan(0, 0, 3, A, B, 10, None) == 1   # bad algo
+    assert lib.ds_scan(0, 0, -1, A, B, 10, None) == 1
+    assert lib.ds_scan(2, 1, 2, A, A + 8, 10, None) == 3
+
+
+def test_compact_validation(lib):
+    C = 0x7F0000200000
+    assert lib.compact_if(9, A, B, C, 10, 0, 0, None) == 2
+    assert lib.compact_if(0, A, B, C, 10, 6, 0, None) == 1   # bad cmp
+    assert lib.compact_if(0, A, B, C, 10, -1, 0, None) == 1
+    assert lib.compact_if(0, A, B, None, 10, 0, 0, None) == 1
+    assert lib.compact_if(0, A, B, C, -3, 0, 0, None) == 1
+    assert lib.compact_if(0, A, B, C + 4, 10, 0, 0, None) == 4
+    assert lib.compact_if(0, A, B, C, 1 << 32, 0, 0, None) == 7
+    assert lib.compact_if(0, A, A + 4, C, 10, 0, 0, None) == 3
+    assert lib.compact_if(0, None, B, C, 10, 0, 0, None) == 1
+
+
+def test_copy_validation(lib):
+    assert lib.ds_copy(A, B, 17, None) == 1
+    assert lib.ds_copy(A, B, -16, None) == 1
+    assert lib.ds_copy(A, B, 0, None) == 0
+    assert lib.ds_copy(A + 4, B, 32, None) == 4
+    assert lib.ds_copy(A, A + 16, 64, None) == 3
+
+
+def test_query_timeout_null(lib):
+    assert lib.ds_query_timeout(None, None) == 1
+
+
+def test_binding_refuses_a_missing_library(tmp_path):
+    from primitives_device_scan_amd import _binding
+    with pytest.raises(ImportError):
+        _binding.load_library(str(tmp_path / "nope.so"))
+
+
+def test_binding_operand_bits():
+    import torch
+    from primitives_device_scan_amd import _binding
+    assert _binding.operand_bits(torch.float32, 1.0) == 0x3F800000
+    assert _binding.operand_bits(torch.int32, -1) == 0xFFFFFFFF
+    assert _binding.operand_bits(torch.int64, -2) == 0xFFFFFFFFFFFFFFFE
