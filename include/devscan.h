@@ -6,7 +6,7 @@
  * work on `stream` and returns without waiting for it. The caller owns every
  * pointer it passes and keeps the memory alive until the stream work is done.
  * The library owns only a small workspace per (device, stream): per-tile
- * status words, a tile ticket counter and, for the three-pass form, the tile
+ * status words, a launch epoch and, for the three-pass form, the tile
  * totals. It grows on demand and is freed by ds_release_workspace().
  *
  * Errors. Argument errors are found on the host before any HIP call and
@@ -74,7 +74,7 @@ typedef enum {
  *   d_out   device pointer to n elements (written); may equal d_in (in place),
  *           must not otherwise overlap it
  *   n       element count, n >= 0; n == 0 enqueues nothing. At most 2^24 - 1
- *           tiles of 16 KiB: 68,719,472,640 four-byte or 34,359,736,320
+ *           tiles of 64 KiB: 274,877,890,560 four-byte or 137,438,945,280
  *           eight-byte elements (DS_ERR_TOO_LARGE beyond)
  *   stream  HIP stream of the current device (0 = null stream)
  * Returns DS_OK or a ds_status error.

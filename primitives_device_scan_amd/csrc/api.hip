@@ -175,7 +175,8 @@ int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected
                    ? DS_OK
                    : DS_ERR_HIP;
     }
-    const int64_t tiles = (n + ds::tile_elems(elem_bytes(dtype)) - 1) / ds::tile_elems(elem_bytes(dtype));
+    const int64_t ct = ds::compact_tile_elems(elem_bytes(dtype));
+    const int64_t tiles = (n + ct - 1) / ct;
     std::lock_guard<std::mutex> lock(g_mu);
     DevWs dws{nullptr, nullptr, nullptr};
     Workspace* w = nullptr;
@@ -198,7 +199,7 @@ int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream)
     if (((uintptr_t)d_in % 16) || ((uintptr_t)d_out % 16)) return DS_ERR_MISALIGNED;
     const uintptr_t a = (uintptr_t)d_in, b = (uintptr_t)d_out, len = (uintptr_t)nbytes;
     if (a < b + len && b < a + len) return DS_ERR_OVERLAP;
-    if (nbytes / ds::kTileBytes >= kMaxTiles) return DS_ERR_TOO_LARGE;
+    if (nbytes / ds::tile_bytes() >= kMaxTiles) return DS_ERR_TOO_LARGE;
     return ds::launch_copy(d_in, d_out, nbytes, stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
@@ -216,13 +217,8 @@ int ds_query_timeout(hipStream_t stream, int* timed_out)
     uint32_t flag = 0;
     if (hipMemcpy(&flag, &c->timeout, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return DS_ERR_HIP;
     if (flag) {
-        // Nothing runs on the stream now: clear the record and restart the
-        // ticket counter, which a give-up leaves right but a corrupted counter
-        // (the other reason the flag is set) would not.
         const uint32_t zero = 0;
-        if (hipMemcpy(&c->timeout, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess ||
-            hipMemcpy(&c->ticket, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
-            return DS_ERR_HIP;
+        if (hipMemcpy(&c->timeout, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return DS_ERR_HIP;
     }
     *timed_out = flag ? 1 : 0;
     return DS_OK;

@@ -26,22 +26,25 @@
 
 namespace ds {
 
+// 16-byte vectors per thread: a scan tile is 256 threads x 16 x 16 B = 64 KiB
+// (16,384 four-byte or 8,192 eight-byte elements). Large tiles keep enough
+// bytes resident per CU for the look-back latency (several microseconds
+// under full HBM load) to hide behind other tiles' transfers. Compaction
+// stages its kept elements in LDS, so it uses 16 KiB tiles.
+constexpr int kVPT = 16;
+constexpr int kCompactVPT = 4;
+constexpr int kTileBytes = kThreads * kVPT * kVecBytes;
+
 namespace {
 
-// Ticket and epoch for this workgroup. Tickets hand out tiles in the order
-// workgroups start, so every tile a workgroup waits for belongs to a
-// workgroup that is already running: the wait always ends.
-__device__ __forceinline__ void take_ticket(Ctrl* ctrl, int64_t& tile, uint32_t& epoch)
-{
-    __shared__ uint32_t s_tile, s_epoch;
-    if (threadIdx.x == 0) {
-        s_tile = __hip_atomic_fetch_add(&ctrl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_epoch = __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    tile = s_tile;
-    epoch = s_epoch;
-}
+// Tile order and forward progress. Tile t is workgroup t (blockIdx.x) and
+// waits only for tiles below t. Workgroups are dispatched in increasing index
+// order (round-robin over the XCDs, in order within each), so the lowest
+// unfinished tile is always running or next to start, and every wait ends.
+// A shared atomic ticket counter would make the order explicit, but every
+// workgroup's fetch-and-add on one address serialises at roughly 50 ns each
+// on this GPU -- over a millisecond for 24,415 tiles -- so the order of the
+// launch is used instead, and the bounded wait in `lookback` backs it up.
 
 __device__ __forceinline__ void flag_timeout(Ctrl* ctrl)
 {
@@ -50,12 +53,16 @@ __device__ __forceinline__ void flag_timeout(Ctrl* ctrl)
 
 // Called by lane 0 of the last tile once it has published its inclusive
 // prefix. Every other tile has by then published a status stamped with the
-// epoch it read (the last tile's prefix depends on all of them), and has
-// taken its ticket, so both words can be advanced for the next launch.
+// epoch it read (the last tile's prefix depends on all of them), so the epoch
+// can be advanced for the next launch.
 __device__ __forceinline__ void end_of_launch(Ctrl* ctrl, uint32_t epoch)
 {
     __hip_atomic_store(&ctrl->epoch, (epoch + 1u) & kEpochMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ctrl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t launch_epoch(Ctrl* ctrl)
+{
+    return __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The exclusive prefix of `tile`, found by wave 0 and shared through LDS.
@@ -83,51 +90,46 @@ __device__ __forceinline__ T tile_prefix(int64_t tile, int64_t num_tiles, uint32
 
 }  // namespace
 
-template <typename T, bool INCLUSIVE, bool VEC>
+template <typename T, bool INCLUSIVE, bool VEC, int VPT>
 __global__ __launch_bounds__(kThreads) void lookback_scan_kernel(const T* in, T* out, int64_t n,
                                                                   int64_t num_tiles, Ctrl* ctrl,
                                                                   uint64_t* status, uint32_t spin_limit)
 {
-    using S = Shape<T>;
+    using S = Shape<T, VPT>;
     constexpr int V = S::kPerVec;
     __shared__ T s_wave[kWaves];
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
 
-    int64_t tile = 0;
-    uint32_t epoch = 0;
-    if (num_tiles > 1) {
-        take_ticket(ctrl, tile, epoch);
-        if (tile >= num_tiles) {  // only if the ticket counter was corrupted
-            if (threadIdx.x == 0) flag_timeout(ctrl);
-            return;
-        }
-    }
+    const int64_t tile = blockIdx.x;
+    // Only wave 0 publishes and looks back; its epoch load overlaps the data loads.
+    const uint32_t epoch = (num_tiles > 1 && wave == 0) ? launch_epoch(ctrl) : 0u;
 
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
     const bool whole = VEC && seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T>(in, seg, lane, e);
+        load_vec<T, VPT>(in, seg, lane, e);
     else
-        load_scalar<T>(in, seg, n, lane, e, T(0));
+        load_scalar<T, VPT>(in, seg, n, lane, e, T(0));
 
-    T off[kVecsPerThread];
+    T off[VPT];
     T wave_excl;
-    const T agg = tile_local_scan<T, V>(e, off, wave_excl, s_wave);
-    const T prefix = num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit) : T(0);
-    tile_finish<T, V, INCLUSIVE>(e, off, wave_excl, prefix);
+    const T agg = tile_local_scan<T, V, VPT>(e, off, wave_excl, s_wave);
+    const T prefix =
+        num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit) : T(0);
+    tile_finish<T, V, VPT, INCLUSIVE>(e, off, wave_excl, prefix);
 
     if (whole)
-        store_vec<T>(out, seg, lane, e);
+        store_vec<T, VPT>(out, seg, lane, e);
     else
-        store_scalar<T>(out, seg, n, lane, e);
+        store_scalar<T, VPT>(out, seg, n, lane, e);
 }
 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void tile_reduce_kernel(const T* in, int64_t n, T* totals)
 {
-    using S = Shape<T>;
+    using S = Shape<T, kVPT>;
     __shared__ T s_wave[kWaves];
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
@@ -135,9 +137,9 @@ __global__ __launch_bounds__(kThreads) void tile_reduce_kernel(const T* in, int6
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
     T e[S::kItems];
     if (VEC && seg + S::kWaveElems <= n)
-        load_vec<T>(in, seg, lane, e);
+        load_vec<T, kVPT>(in, seg, lane, e);
     else
-        load_scalar<T>(in, seg, n, lane, e, T(0));
+        load_scalar<T, kVPT>(in, seg, n, lane, e, T(0));
     T s = T(0);
 #pragma unroll
     for (int i = 0; i < S::kItems; ++i) s = s + e[i];
@@ -187,7 +189,7 @@ template <typename T, bool INCLUSIVE, bool VEC>
 __global__ __launch_bounds__(kThreads) void tile_rescan_kernel(const T* in, T* out, int64_t n,
                                                                 const T* offsets)
 {
-    using S = Shape<T>;
+    using S = Shape<T, kVPT>;
     constexpr int V = S::kPerVec;
     __shared__ T s_wave[kWaves];
     const int lane = lane_id();
@@ -197,17 +199,17 @@ __global__ __launch_bounds__(kThreads) void tile_rescan_kernel(const T* in, T* o
     const bool whole = VEC && seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T>(in, seg, lane, e);
+        load_vec<T, kVPT>(in, seg, lane, e);
     else
-        load_scalar<T>(in, seg, n, lane, e, T(0));
-    T off[kVecsPerThread];
+        load_scalar<T, kVPT>(in, seg, n, lane, e, T(0));
+    T off[kVPT];
     T wave_excl;
-    tile_local_scan<T, V>(e, off, wave_excl, s_wave);
-    tile_finish<T, V, INCLUSIVE>(e, off, wave_excl, offsets[tile]);
+    tile_local_scan<T, V, kVPT>(e, off, wave_excl, s_wave);
+    tile_finish<T, V, kVPT, INCLUSIVE>(e, off, wave_excl, offsets[tile]);
     if (whole)
-        store_vec<T>(out, seg, lane, e);
+        store_vec<T, kVPT>(out, seg, lane, e);
     else
-        store_scalar<T>(out, seg, n, lane, e);
+        store_scalar<T, kVPT>(out, seg, n, lane, e);
 }
 
 template <typename T>
@@ -228,48 +230,41 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(const T* in, T* out, 
                                                             int64_t n, int64_t num_tiles, int cmp, T operand,
                                                             Ctrl* ctrl, uint64_t* status, uint32_t spin_limit)
 {
-    using S = Shape<T>;
+    using S = Shape<T, kCompactVPT>;
     constexpr int V = S::kPerVec;
     __shared__ uint32_t s_wave[kWaves];
     __shared__ T s_stage[S::kTile];
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
 
-    int64_t tile = 0;
-    uint32_t epoch = 0;
-    if (num_tiles > 1) {
-        take_ticket(ctrl, tile, epoch);
-        if (tile >= num_tiles) {  // only if the ticket counter was corrupted
-            if (threadIdx.x == 0) flag_timeout(ctrl);
-            return;
-        }
-    }
+    const int64_t tile = blockIdx.x;
+    const uint32_t epoch = (num_tiles > 1 && wave == 0) ? launch_epoch(ctrl) : 0u;
 
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
     const bool whole = VEC && seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T>(in, seg, lane, e);
+        load_vec<T, kCompactVPT>(in, seg, lane, e);
     else
-        load_scalar<T>(in, seg, n, lane, e, T(0));
+        load_scalar<T, kCompactVPT>(in, seg, n, lane, e, T(0));
 
     uint32_t cnt[S::kItems];
     bool kept[S::kItems];
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
+    for (int k = 0; k < kCompactVPT; ++k)
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             const int i = k * V + j;
             kept[i] = (whole || elem_index<T>(seg, k, j, lane) < n) && keep(e[i], cmp, operand);
             cnt[i] = kept[i] ? 1u : 0u;
         }
-    uint32_t off[kVecsPerThread];
+    uint32_t off[kCompactVPT];
     uint32_t wave_excl;
-    const uint32_t agg = tile_local_scan<uint32_t, V>(cnt, off, wave_excl, s_wave);
+    const uint32_t agg = tile_local_scan<uint32_t, V, kCompactVPT>(cnt, off, wave_excl, s_wave);
 
     // Stage kept elements at their rank inside the tile (memory order).
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
+    for (int k = 0; k < kCompactVPT; ++k)
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             const int i = k * V + j;
@@ -291,16 +286,17 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(const T* in, T* out, 
     if (tile == num_tiles - 1 && threadIdx.x == 0) *num_selected = (int64_t)prefix + agg;
 }
 
+template <int VPT>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* in, u32x4* out, int64_t nvec)
 {
-    const int64_t base = (int64_t)blockIdx.x * (kThreads * kVecsPerThread) +
-                         (int64_t)(threadIdx.x / kWave) * (kWave * kVecsPerThread) + lane_id();
-    u32x4 r[kVecsPerThread];
+    const int64_t base = (int64_t)blockIdx.x * (kThreads * VPT) +
+                         (int64_t)(threadIdx.x / kWave) * (kWave * VPT) + lane_id();
+    u32x4 r[VPT];
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
+    for (int k = 0; k < VPT; ++k)
         if (base + k * kWave < nvec) r[k] = __builtin_nontemporal_load(in + base + k * kWave);
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
+    for (int k = 0; k < VPT; ++k)
         if (base + k * kWave < nvec) __builtin_nontemporal_store(r[k], out + base + k * kWave);
 }
 
@@ -308,6 +304,8 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* in, u32x4* 
 // Launchers.
 // ---------------------------------------------------------------------------
 int64_t tile_elems(int elem_bytes) { return (int64_t)kTileBytes / elem_bytes; }
+int64_t tile_bytes() { return kTileBytes; }
+int64_t compact_tile_elems(int elem_bytes) { return (int64_t)kThreads * kCompactVPT * kVecBytes / elem_bytes; }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -315,8 +313,8 @@ template <typename T, bool INCL, bool VEC>
 static hipError_t lookback_typed(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
                                  hipStream_t st)
 {
-    const int64_t tiles = (n + Shape<T>::kTile - 1) / Shape<T>::kTile;
-    lookback_scan_kernel<T, INCL, VEC><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
+    lookback_scan_kernel<T, INCL, VEC, kVPT><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
         (const T*)in, (T*)out, n, tiles, ws.ctrl, ws.status, spin);
     return hipGetLastError();
 }
@@ -348,7 +346,7 @@ template <typename T, bool VEC>
 static hipError_t three_pass_typed(bool incl, const void* in, void* out, int64_t n, const DevWs& ws,
                                    hipStream_t st)
 {
-    const int64_t tiles = (n + Shape<T>::kTile - 1) / Shape<T>::kTile;
+    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
     T* totals = (T*)ws.totals;
     tile_reduce_kernel<T, VEC><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>((const T*)in, n, totals);
     hipError_t e = hipGetLastError();
@@ -388,7 +386,7 @@ template <typename T>
 static hipError_t compact_typed(const void* in, void* out, int64_t* num_selected, int64_t n, int cmp,
                                 uint64_t operand_bits, const DevWs& ws, uint32_t spin, hipStream_t st)
 {
-    const int64_t tiles = (n + Shape<T>::kTile - 1) / Shape<T>::kTile;
+    const int64_t tiles = (n + Shape<T, kCompactVPT>::kTile - 1) / Shape<T, kCompactVPT>::kTile;
     T operand;
     if constexpr (sizeof(T) == 4)
         operand = __builtin_bit_cast(T, (uint32_t)operand_bits);
@@ -418,9 +416,9 @@ hipError_t launch_compact(ElemKind kind, const void* in, void* out, int64_t* num
 hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t stream)
 {
     const int64_t nvec = nbytes / kVecBytes;
-    const int64_t per_block = (int64_t)kThreads * kVecsPerThread;
+    const int64_t per_block = (int64_t)kThreads * kVPT;
     const int64_t blocks = (nvec + per_block - 1) / per_block;
-    copy_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>((const u32x4*)in, (u32x4*)out, nvec);
+    copy_kernel<kVPT><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>((const u32x4*)in, (u32x4*)out, nvec);
     return hipGetLastError();
 }
 

@@ -11,14 +11,16 @@ struct Ctrl;
 
 // Device memory of one workspace.
 struct DevWs {
-    Ctrl* ctrl;          // control words (ticket, epoch, timeout)
+    Ctrl* ctrl;          // control words (epoch, give-up flag)
     uint64_t* status;    // 2 x 64-bit words per tile (look-back status)
     void* totals;        // 8 bytes per tile (three-pass tile totals)
 };
 
 enum ElemKind { kU32 = 0, kF32 = 1, kU64 = 2, kI32 = 3, kI64 = 4 };
 
-int64_t tile_elems(int elem_bytes);
+int64_t tile_elems(int elem_bytes);          // scan tile
+int64_t compact_tile_elems(int elem_bytes);  // compaction tile
+int64_t tile_bytes();
 
 hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
                                 const DevWs& ws, uint32_t spin_limit, hipStream_t stream);

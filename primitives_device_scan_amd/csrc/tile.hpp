@@ -19,26 +19,25 @@ namespace ds {
 constexpr int kWave = 64;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kVecsPerThread = 4;
 constexpr int kVecBytes = 16;
-constexpr int kTileBytes = kThreads * kVecsPerThread * kVecBytes;  // 16 KiB
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte access
 
-template <typename T>
+// VPT = 16-byte vectors per thread; the tile is kThreads * VPT * 16 bytes.
+template <typename T, int VPT>
 struct Shape {
     static constexpr int kPerVec = kVecBytes / (int)sizeof(T);   // elements per 16-byte vector
-    static constexpr int kItems = kPerVec * kVecsPerThread;      // elements per thread
+    static constexpr int kItems = kPerVec * VPT;                 // elements per thread
     static constexpr int kWaveElems = kWave * kItems;            // elements per wave
     static constexpr int kTile = kThreads * kItems;              // elements per tile
+    static constexpr int kTileBytes = kThreads * VPT * kVecBytes;
 };
 
 // Launch-wide control words, kept in the workspace.
 struct Ctrl {
-    uint32_t ticket;    // next tile ticket; the last tile of a launch resets it to 0
     uint32_t epoch;     // 30-bit launch number stamped into status words
     uint32_t timeout;   // set to 1 when a look-back wait gave up
-    uint32_t pad[61];
+    uint32_t pad[62];
 };
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
@@ -107,59 +106,61 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_bal
 template <typename T>
 __device__ __forceinline__ int64_t elem_index(int64_t seg, int k, int j, int lane)
 {
-    return seg + (int64_t)(k * kWave + lane) * Shape<T>::kPerVec + j;
+    return seg + (int64_t)(k * kWave + lane) * (kVecBytes / (int)sizeof(T)) + j;
 }
 
 // Whole wave segment in range and 16-byte aligned: one 16-byte load per vector.
-template <typename T>
+template <typename T, int VPT>
 __device__ __forceinline__ void load_vec(const T* __restrict__ in, int64_t seg, int lane,
-                                         T (&e)[Shape<T>::kItems])
+                                         T (&e)[Shape<T, VPT>::kItems])
 {
     const u32x4* p = reinterpret_cast<const u32x4*>(in + seg) + lane;
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k) {
+    for (int k = 0; k < VPT; ++k) {
         const u32x4 r = __builtin_nontemporal_load(p + k * kWave);
-        __builtin_memcpy(&e[k * Shape<T>::kPerVec], &r, kVecBytes);
+        __builtin_memcpy(&e[k * Shape<T, VPT>::kPerVec], &r, kVecBytes);
     }
 }
 
 // Element-wise, guarded: elements at or past n read as `fill`.
-template <typename T>
+template <typename T, int VPT>
 __device__ __forceinline__ void load_scalar(const T* __restrict__ in, int64_t seg, int64_t n, int lane,
-                                            T (&e)[Shape<T>::kItems], T fill)
+                                            T (&e)[Shape<T, VPT>::kItems], T fill)
 {
+    constexpr int V = Shape<T, VPT>::kPerVec;
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
+    for (int k = 0; k < VPT; ++k)
 #pragma unroll
-        for (int j = 0; j < Shape<T>::kPerVec; ++j) {
+        for (int j = 0; j < V; ++j) {
             const int64_t i = elem_index<T>(seg, k, j, lane);
-            e[k * Shape<T>::kPerVec + j] = i < n ? in[i] : fill;
+            e[k * V + j] = i < n ? in[i] : fill;
         }
 }
 
-template <typename T>
+template <typename T, int VPT>
 __device__ __forceinline__ void store_vec(T* __restrict__ out, int64_t seg, int lane,
-                                          const T (&e)[Shape<T>::kItems])
+                                          const T (&e)[Shape<T, VPT>::kItems])
 {
     u32x4* p = reinterpret_cast<u32x4*>(out + seg) + lane;
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k) {
+    for (int k = 0; k < VPT; ++k) {
         u32x4 r;
-        __builtin_memcpy(&r, &e[k * Shape<T>::kPerVec], kVecBytes);
+        __builtin_memcpy(&r, &e[k * Shape<T, VPT>::kPerVec], kVecBytes);
         __builtin_nontemporal_store(r, p + k * kWave);
     }
 }
 
-template <typename T>
+template <typename T, int VPT>
 __device__ __forceinline__ void store_scalar(T* __restrict__ out, int64_t seg, int64_t n, int lane,
-                                             const T (&e)[Shape<T>::kItems])
+                                             const T (&e)[Shape<T, VPT>::kItems])
 {
+    constexpr int V = Shape<T, VPT>::kPerVec;
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
+    for (int k = 0; k < VPT; ++k)
 #pragma unroll
-        for (int j = 0; j < Shape<T>::kPerVec; ++j) {
+        for (int j = 0; j < V; ++j) {
             const int64_t i = elem_index<T>(seg, k, j, lane);
-            if (i < n) out[i] = e[k * Shape<T>::kPerVec + j];
+            if (i < n) out[i] = e[k * V + j];
         }
 }
 
@@ -174,26 +175,25 @@ __device__ __forceinline__ void store_scalar(T* __restrict__ out, int64_t seg, i
 // one, return value = the tile aggregate. s_wave is kWaves values of LDS.
 // Contains one workgroup barrier.
 // ---------------------------------------------------------------------------
-template <typename T, int V>
-__device__ __forceinline__ T tile_local_scan(T (&e)[V * kVecsPerThread], T (&off)[kVecsPerThread],
-                                             T& wave_excl, T* s_wave)
+template <typename T, int V, int VPT>
+__device__ __forceinline__ T tile_local_scan(T (&e)[V * VPT], T (&off)[VPT], T& wave_excl, T* s_wave)
 {
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
+    for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int j = 1; j < V; ++j)
             e[k * V + j] = e[k * V + j] + e[k * V + j - 1];
 
-    T incl[kVecsPerThread];
+    T incl[VPT];
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k)
+    for (int k = 0; k < VPT; ++k)
         incl[k] = wave_inclusive_scan(e[k * V + V - 1]);
 
     T run = T(0);
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k) {
+    for (int k = 0; k < VPT; ++k) {
         off[k] = run + wave_shift_right1(incl[k]);
         run = run + readlane(incl[k], kWave - 1);
     }
@@ -211,13 +211,12 @@ __device__ __forceinline__ T tile_local_scan(T (&e)[V * kVecsPerThread], T (&off
 }
 
 // Final values from the local scan and the tile's exclusive prefix.
-template <typename T, int V, bool INCLUSIVE>
-__device__ __forceinline__ void tile_finish(T (&e)[V * kVecsPerThread], const T (&off)[kVecsPerThread],
-                                            T wave_excl, T prefix)
+template <typename T, int V, int VPT, bool INCLUSIVE>
+__device__ __forceinline__ void tile_finish(T (&e)[V * VPT], const T (&off)[VPT], T wave_excl, T prefix)
 {
     const T head = prefix + wave_excl;
 #pragma unroll
-    for (int k = 0; k < kVecsPerThread; ++k) {
+    for (int k = 0; k < VPT; ++k) {
         const T base = head + off[k];
         if constexpr (INCLUSIVE) {
 #pragma unroll
@@ -300,14 +299,20 @@ struct StatusCodec {
     }
 };
 
-// Decoupled look-back, run by one whole wave for tile `tile` (> 0) after the
-// tile's aggregate is known. Publishes the aggregate, then reads the status of
-// the 64 preceding tiles at once (lane l reads tile - 1 - l), waits while any
-// tile up to the nearest inclusive prefix has published nothing, adds the
-// aggregates and that prefix, and moves 64 tiles further back when the window
-// holds no prefix. Publishes this tile's inclusive prefix and returns the
-// exclusive one. A wait that exceeds `spin_limit` polls gives up: the missing
-// values count as 0 and `timeout` is set, so every wave still finishes.
+// Decoupled look-back, run by one whole wave for tile `tile` (> 0) once the
+// tile's aggregate is known.
+//  1. Publish the aggregate.
+//  2. Wait, polling with lane 0 alone, until the nearest predecessor has
+//     published anything: until then no window can complete, and polling one
+//     word instead of 64 keeps the status traffic off the memory system.
+//  3. Read the status of the 64 preceding tiles at once (lane l reads tile
+//     base - l, one coalesced 512-byte access), re-read only the words that
+//     still show nothing up to the nearest inclusive prefix, add the
+//     aggregates and that prefix, and move 64 tiles further back when the
+//     window holds no prefix.
+//  4. Publish this tile's inclusive prefix; return the exclusive one.
+// Every wait is bounded: after `spin_limit` polls in total the wave gives up,
+// missing values count as 0 and `timeout` is set, so every wave finishes.
 template <typename T>
 __device__ T lookback(uint64_t* status, int64_t tile, uint32_t epoch, T agg, uint32_t spin_limit,
                       uint32_t* timeout)
@@ -315,33 +320,52 @@ __device__ T lookback(uint64_t* status, int64_t tile, uint32_t epoch, T agg, uin
     using C = StatusCodec<T>;
     const int lane = lane_id();
     if (lane == 0) C::publish(status, tile, epoch, kFlagAggregate, agg);
-    T acc = T(0);
-    int64_t base = tile - 1;
     uint32_t polls = 0;
     bool gave_up = false;
+    auto give_up = [&]() {
+        gave_up = true;
+        if (lane == 0) __hip_atomic_store(timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    for (;;) {
+        uint32_t f = kFlagPrefix;
+        T v0;
+        if (lane == 0) f = C::read(status, tile - 1, epoch, v0);
+        if (__builtin_amdgcn_readfirstlane(f) != kFlagNone) break;
+        if (++polls >= spin_limit) {
+            give_up();
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    T acc = T(0);
+    int64_t base = tile - 1;
     for (;;) {
         const int64_t idx = base - lane;
         T v = T(0);
         uint32_t flag = kFlagPrefix;  // before tile 0: an inclusive prefix of 0
         if (idx >= 0) flag = C::read(status, idx, epoch, v);
-        const uint64_t pm = ballot(flag == kFlagPrefix);
-        const uint64_t xm = ballot(flag == kFlagNone);
-        const uint64_t upto = pm ? (pm ^ (pm - 1)) : ~0ull;  // lanes up to the first prefix
-        if ((xm & upto) && !gave_up) {
-            if (++polls < spin_limit) {
-                __builtin_amdgcn_s_sleep(1);
-                continue;
+        for (;;) {
+            const uint64_t pm = ballot(flag == kFlagPrefix);
+            const uint64_t xm = ballot(flag == kFlagNone);
+            const uint64_t upto = pm ? (pm ^ (pm - 1)) : ~0ull;  // lanes up to the first prefix
+            const bool needed = (upto >> lane) & 1ull;
+            if ((xm & upto) && !gave_up) {
+                if (++polls < spin_limit) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (needed && flag == kFlagNone) flag = C::read(status, idx, epoch, v);
+                    continue;
+                }
+                give_up();
             }
-            gave_up = true;
-            if (lane == 0) __hip_atomic_store(timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            acc = acc + wave_sum((needed && flag != kFlagNone) ? v : T(0));
+            if (pm) {
+                if (lane == 0) C::publish(status, tile, epoch, kFlagPrefix, acc + agg);
+                return acc;
+            }
+            break;
         }
-        const bool take = ((upto >> lane) & 1ull) && flag != kFlagNone;
-        acc = acc + wave_sum(take ? v : T(0));
-        if (pm) break;
         base -= kWave;
     }
-    if (lane == 0) C::publish(status, tile, epoch, kFlagPrefix, acc + agg);
-    return acc;
 }
 
 }  // namespace ds

@@ -93,8 +93,12 @@ def gpu_compact(x: np.ndarray, op: str, operand, in_place: bool = False):
     return from_dev(out, x.dtype, 0, n), k
 
 
-def tile_of(dtype) -> int:
-    return 16384 // np.dtype(dtype).itemsize
+SCAN_TILE_BYTES = 65536     # one scan workgroup's tile
+COMPACT_TILE_BYTES = 16384  # one compaction workgroup's tile
+
+
+def tile_of(dtype, compact: bool = False) -> int:
+    return (COMPACT_TILE_BYTES if compact else SCAN_TILE_BYTES) // np.dtype(dtype).itemsize
 
 
 def assert_int_equal(got: np.ndarray, want: np.ndarray, what: str):

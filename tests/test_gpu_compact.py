@@ -26,7 +26,7 @@ def test_compact_256m_keys_below_2_31():
 @pytest.mark.parametrize("case", range(len(pins.COMPACT_CASES)))
 def test_compact_dtypes_ops(case):
     dt, gen, operands = pins.COMPACT_CASES[case]
-    T = tile_of(dt)
+    T = tile_of(dt, compact=True)
     for n in (1, 7, 64, T - 1, T, T + 1, 3 * T + 5, 70 * T + 3):
         x = gen(500 + n, n).astype(dt)
         for c in operands:
@@ -52,7 +52,7 @@ def test_compact_nan_and_edges():
 
 
 def test_compact_in_place():
-    n = 40 * tile_of(np.uint32) + 17
+    n = 40 * tile_of(np.uint32, compact=True) + 17
     x = datagen.keys_u32(31, n)
     out, k = gpu_compact(x, ">=", 3 << 30, in_place=True)
     want = oracle.compact(x, ">=", 3 << 30)
@@ -61,7 +61,7 @@ def test_compact_in_place():
 
 
 def test_compact_all_and_none():
-    n = 9 * tile_of(np.int32) + 1
+    n = 9 * tile_of(np.int32, compact=True) + 1
     x = datagen.uniform_int(8, n, 0, 9)
     out, k = gpu_compact(x, ">=", 0)
     assert k == n and np.array_equal(out[:k], x)

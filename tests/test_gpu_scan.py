@@ -45,7 +45,7 @@ def test_worked_examples(dt, algo):
 
 def test_one_tile_int32_exclusive():
     x = cached_workload("one_tile")
-    assert x.size == tile_of(np.int32)
+    assert x.size <= tile_of(np.int32)  # one workgroup, no look-back
     say("one_tile int32 exclusive n=4096 (single workgroup)")
     check_scan(x, False, gpu_scan(x, False), "one_tile")
     check_scan(x, False, gpu_scan(x, False, entry="scan_exclusive"), "one_tile via scan_exclusive")
@@ -190,9 +190,9 @@ def test_binding_entry_points():
     assert ds.scan(x, False, algo="three_pass").tolist() == [0, 3, 4, 11, 11, 15, 16, 22]
     e = torch.empty(0, dtype=torch.float32, device="cuda")
     assert ds.scan_exclusive(e).numel() == 0
-    with pytest.raises(ds.DevscanError):
-        ds.scan_exclusive(torch.zeros(100, dtype=torch.int32, device="cuda")[1:],
-                          torch.zeros(100, dtype=torch.int32, device="cuda")[:99].view(torch.int32))
+    buf = torch.zeros(100, dtype=torch.int32, device="cuda")
+    with pytest.raises(ds.DevscanError):  # partial overlap is refused before any launch
+        ds.scan_exclusive(buf[1:], buf[:99])
     with pytest.raises(TypeError):
         ds.scan_exclusive(torch.zeros(8, dtype=torch.float16, device="cuda"))
 
@@ -201,7 +201,7 @@ def test_give_up_path_then_recovery():
     """A tiny spin limit makes look-back waits give up (outputs invalid, flag
     set) while every kernel still finishes; later calls are correct again."""
     import primitives_device_scan_amd as ds
-    n = 600 * tile_of(np.int32) + 9
+    n = 300 * tile_of(np.int32) + 9
     x = datagen.uniform_int(5, n, 0, 9)
     ds.query_timeout()  # clear
     ds.set_spin_limit(1)
