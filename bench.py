@@ -56,6 +56,23 @@ def measured_traffic(per_launch_alg_bytes: float):
     return t["hbm_bytes_per_launch"]
 
 
+def check_outputs(x_i, x_f, d_yi, d_yf) -> float:
+    """Exits unless the int32 scan equals the oracle's and the fp32 scan is
+    within 1e-5 * sum|x| of the fp64 oracle; returns the fp32 max |err|/S."""
+    import numpy as np
+
+    import oracle
+    if not np.array_equal(d_yi.cpu().numpy(), oracle.scan(x_i, False)):
+        log("int32 scan differs from the oracle")
+        sys.exit(1)
+    y, s = oracle.scan(x_f, False)
+    ratio = float(np.max(np.abs(d_yf.cpu().numpy().astype(np.float64) - y) / np.maximum(s, 1e-300)))
+    if not ratio <= 1e-5:
+        log(f"fp32 scan outside tolerance: max |err|/S = {ratio}")
+        sys.exit(1)
+    return ratio
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -65,7 +82,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--compact", action="store_true", help="also time compact_if on 268,435,456 uint32 keys")
     ap.add_argument("--profile-only", action="store_true",
-                    help="inputs, one check, then --steps scans; no extras (for rocprofv3 runs)")
+                    help="inputs, one check, then --steps scans and --steps copies; no timing (for rocprofv3 runs)")
+    ap.add_argument("--no-check", action="store_true", help="with --profile-only: skip the oracle check")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -107,29 +125,31 @@ def main():
             raise ds.DevscanError(st, "scan_exclusive fp32")
 
     # Check before timing: the oracle on the same bytes.
-    import oracle
-    log("checking against the oracle")
     scan_i()
     scan_f()
     torch.cuda.synchronize()
-    if not np.array_equal(d_yi.cpu().numpy(), oracle.scan(x_i, False)):
-        log("int32 scan differs from the oracle")
-        sys.exit(1)
-    y, s = oracle.scan(x_f, False)
-    ratio = float(np.max(np.abs(d_yf.cpu().numpy().astype(np.float64) - y) / np.maximum(s, 1e-300)))
-    del y, s
-    if not ratio <= 1e-5:
-        log(f"fp32 scan outside tolerance: max |err|/S = {ratio}")
-        sys.exit(1)
+    ratio = None
+    if args.no_check and args.profile_only:
+        log("(oracle check skipped for a counter run)")
+    else:
+        log("checking against the oracle")
+        ratio = check_outputs(x_i, x_f, d_yi, d_yf)
     if ds.query_timeout():
         log("a look-back wait gave up")
         sys.exit(1)
 
     K, W = args.steps, args.warmup
     if args.profile_only:
+        # Scans, then the same-pattern copy of a known size (n*4 bytes read,
+        # n*4 bytes written per launch; n*4 rounded down to 16 bytes), whose
+        # counters give the scale factor for the scans' FETCH/WRITE_SIZE.
         for _ in range(K):
             scan_i()
             scan_f()
+        for _ in range(K):
+            st = L.ds_copy(d_xi.data_ptr(), d_yi.data_ptr(), n * 4 // 16 * 16, sh)
+            if st:
+                raise ds.DevscanError(st, "ds_copy")
         torch.cuda.synchronize()
         log("profile run done")
         return
