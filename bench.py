@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "scan G-elem/s and achieved HBM GB/s (% of peak) at n=100M fp32/int32"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lookback_scan_100m.json")
-KERNEL_SOURCES = ["primitives_device_scan_amd/csrc/tile.hpp", "primitives_device_scan_amd/csrc/kernels.hip"]
+KERNEL_SOURCES = ["primitives_device_scan_amd/csrc/tile.hpp", "primitives_device_scan_amd/csrc/device_scan.hpp",
+                  "primitives_device_scan_amd/csrc/scan_lookback.hip"]
 
 
 def log(*a):
@@ -232,6 +233,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         log(f"timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
+        import oracle
         orc = oracle.default()
         yi = np.empty_like(x_i)
         yf = np.empty(n, dtype=np.float64)

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdevscan.so")
-SOURCES = ["kernels.hip", "api.hip"]
+SOURCES = ["scan_lookback.hip", "scan_three_pass.hip", "compact.hip", "copy.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -28,14 +28,17 @@ def hipcc_flags(extra=()):
 
 
 def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
-    objs = []
-    for src in SOURCES:
+    objs, procs = [], []
+    for src in SOURCES:  # compile the sources in parallel
         obj = os.path.join(CSRC, src + ".o")
         cmd = [HIPCC, *hipcc_flags(extra), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
         objs.append(obj)
+    for cmd, p in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(p.returncode, cmd)
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -1,0 +1,166 @@
+// compact.hip -- order-preserving stream compaction in one pass: keep flags
+// counted per tile, the counts scanned with the same look-back as the scan,
+// kept elements written contiguously at their global rank ("Prefix sum and
+// other parallel patterns", section "Stream compaction", first exercise,
+// fused form).
+#include "device_scan.hpp"
+
+namespace ds {
+
+// The comparison as three compares and launch-uniform masks, no branch per
+// element: keep = (lt & m.lt) | (gt & m.gt) | (eq & m.eq) | (!eq & m.ne).
+// With lt = v < c, gt = c < v, eq = v == c this gives < <= > >= == != in the
+// element type's own order; a NaN has lt = gt = eq = false, so it is kept
+// only under !=.
+struct CmpMask {
+    bool lt, gt, eq, ne;
+};
+
+__host__ __device__ inline CmpMask cmp_mask(int cmp)
+{
+    return CmpMask{cmp == 0 || cmp == 1, cmp == 2 || cmp == 3, cmp == 1 || cmp == 3 || cmp == 4, cmp == 5};
+}
+
+template <typename T>
+__device__ __forceinline__ bool keep(T v, CmpMask m, T c)
+{
+    const bool lt = v < c, gt = c < v, eq = v == c;
+    return (lt && m.lt) || (gt && m.gt) || (eq && m.eq) || (!eq && m.ne);
+}
+
+// Compaction over the scan's 64 KiB tiles. The keep flags live as one bit per
+// element in a 64-bit mask; the per-vector keep counts go through the same
+// wave/tile scan and look-back as a scan of 32-bit counts. Once the tile's
+// output offset is known, each wave moves its kept elements out in rounds of
+// kGroup vector indices: the kept elements of those slices are packed into a
+// per-wave LDS buffer at their rank -- shifted so that LDS index and output
+// index agree modulo a 16-byte vector -- and written back as one contiguous
+// run of 16-byte non-temporal stores (element stores at the two ragged ends).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+}
+
+constexpr int kGroup = 8;  // vector indices per staging round: 8 KiB of LDS per wave
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* out, int64_t* num_selected,
+                                                               int64_t n, int64_t num_tiles, int cmp, T operand,
+                                                               Ctrl* ctrl, uint64_t* status, uint32_t spin_limit)
+{
+    using S = Shape<T, kVPT>;
+    constexpr int V = S::kPerVec;
+    constexpr int kBuf = kWave * V * kGroup + V;  // a round's slices plus the alignment shift
+    static_assert(S::kItems <= 64, "keep mask is 64 bits");
+    static_assert(kVPT % kGroup == 0, "whole rounds");
+    __shared__ uint32_t s_wave[kWaves];
+    __shared__ __attribute__((aligned(16))) T s_stage[kWaves][kBuf];
+    const int lane = lane_id();
+    const int wave = (int)(threadIdx.x / kWave);
+    const int64_t tile = blockIdx.x;
+    const uint32_t epoch = (num_tiles > 1 && wave == 0) ? launch_epoch(ctrl) : 0u;
+
+    const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
+    const bool whole = VEC && seg + S::kWaveElems <= n;
+    T e[S::kItems];
+    if (whole)
+        load_vec<T, kVPT>(in, seg, lane, e);
+    else
+        load_scalar<T, kVPT>(in, seg, n, lane, e, T(0));
+
+    const CmpMask m = cmp_mask(cmp);
+    uint64_t keepm = 0;
+#pragma unroll
+    for (int k = 0; k < kVPT; ++k)
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const int i = k * V + j;
+            if ((whole || elem_index<T>(seg, k, j, lane) < n) && keep(e[i], m, operand)) keepm |= 1ull << i;
+        }
+    uint32_t cnt[kVPT];
+#pragma unroll
+    for (int k = 0; k < kVPT; ++k)
+        cnt[k] = (uint32_t)__builtin_popcountll((keepm >> (k * V)) & ((1ull << V) - 1));
+    uint32_t off[kVPT];
+    uint32_t wave_excl;
+    const uint32_t agg = tile_local_scan<uint32_t, 1, kVPT>(cnt, off, wave_excl, s_wave);
+    const uint32_t wave_total = s_wave[wave];
+
+    uint32_t prefix = 0;
+    if (num_tiles > 1)
+        prefix = tile_prefix<uint32_t>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit);
+
+    // A prefix past n can only come from a look-back that gave up; never write past the buffer.
+    const bool fits = (int64_t)prefix + agg <= n;
+    if (!fits && threadIdx.x == 0) flag_timeout(ctrl);
+    const int64_t wave_base = (int64_t)prefix + wave_excl;  // output index of this wave's first kept element
+    T* const stage = s_stage[wave];
+#pragma unroll
+    for (int g = 0; g < kVPT; g += kGroup) {
+        const uint32_t start = readlane(off[g], 0);  // rank of the round's first kept element in the wave
+        const uint32_t end = g + kGroup < kVPT ? readlane(off[g + kGroup], 0) : wave_total;
+        const int64_t first = wave_base + start;
+        const uint32_t shift = VEC ? (uint32_t)(first % V) : 0u;
+#pragma unroll
+        for (int k = g; k < g + kGroup; ++k) {
+            uint32_t r = off[k] - start + shift;
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                if ((keepm >> (k * V + j)) & 1ull) stage[r++] = e[k * V + j];
+        }
+        wave_lds_sync();
+        const uint32_t span = shift + (end - start);  // staged slots, the shift included
+        T* const dst = out + (first - shift);         // 16-byte aligned when VEC
+        if (fits) {
+            if (VEC) {
+                for (uint32_t q = (uint32_t)lane * V; q < span; q += kWave * V) {
+                    if (q >= shift && q + V <= span) {
+                        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + q),
+                                                    reinterpret_cast<u32x4*>(dst + q));
+                    } else {
+                        for (uint32_t i = q; i < q + V && i < span; ++i)
+                            if (i >= shift) dst[i] = stage[i];
+                    }
+                }
+            } else {
+                for (uint32_t i = lane; i < span; i += kWave) dst[i] = stage[i];
+            }
+        }
+        wave_lds_sync();
+    }
+    if (tile == num_tiles - 1 && threadIdx.x == 0) *num_selected = (int64_t)prefix + agg;
+}
+
+template <typename T>
+static hipError_t compact_typed(const void* in, void* out, int64_t* num_selected, int64_t n, int cmp,
+                                uint64_t operand_bits, const DevWs& ws, uint32_t spin, hipStream_t st)
+{
+    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
+    T operand;
+    if constexpr (sizeof(T) == 4)
+        operand = __builtin_bit_cast(T, (uint32_t)operand_bits);
+    else
+        operand = __builtin_bit_cast(T, operand_bits);
+    if (aligned16(in) && aligned16(out))
+        compact_kernel<T, true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+            (const T*)in, (T*)out, num_selected, n, tiles, cmp, operand, ws.ctrl, ws.status, spin);
+    else
+        compact_kernel<T, false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+            (const T*)in, (T*)out, num_selected, n, tiles, cmp, operand, ws.ctrl, ws.status, spin);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact(ElemKind kind, const void* in, void* out, int64_t* num_selected, int64_t n, int cmp,
+                          uint64_t operand_bits, const DevWs& ws, uint32_t spin_limit, hipStream_t stream)
+{
+    switch (kind) {
+    case kU32: return compact_typed<uint32_t>(in, out, num_selected, n, cmp, operand_bits, ws, spin_limit, stream);
+    case kI32: return compact_typed<int32_t>(in, out, num_selected, n, cmp, operand_bits, ws, spin_limit, stream);
+    case kF32: return compact_typed<float>(in, out, num_selected, n, cmp, operand_bits, ws, spin_limit, stream);
+    case kU64: return compact_typed<uint64_t>(in, out, num_selected, n, cmp, operand_bits, ws, spin_limit, stream);
+    default: return compact_typed<int64_t>(in, out, num_selected, n, cmp, operand_bits, ws, spin_limit, stream);
+    }
+}
+
+}  // namespace ds

@@ -1,0 +1,79 @@
+// scan_lookback.hip -- the single-pass device-wide scan: each tile scans
+// itself in registers, publishes its aggregate, looks back over the status of
+// earlier tiles for its exclusive prefix, publishes its inclusive prefix and
+// writes ("Prefix sum and other parallel patterns", section "A device-level
+// scan: scan then propagate", decoupled look-back).
+#include "device_scan.hpp"
+
+namespace ds {
+
+template <typename T, bool INCLUSIVE, bool VEC, int VPT>
+__global__ __launch_bounds__(kThreads) void lookback_scan_kernel(const T* in, T* out, int64_t n,
+                                                                  int64_t num_tiles, Ctrl* ctrl,
+                                                                  uint64_t* status, uint32_t spin_limit)
+{
+    using S = Shape<T, VPT>;
+    constexpr int V = S::kPerVec;
+    __shared__ T s_wave[kWaves];
+    const int lane = lane_id();
+    const int wave = (int)(threadIdx.x / kWave);
+
+    const int64_t tile = blockIdx.x;
+    // Only wave 0 publishes and looks back; its epoch load overlaps the data loads.
+    const uint32_t epoch = (num_tiles > 1 && wave == 0) ? launch_epoch(ctrl) : 0u;
+
+    const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
+    const bool whole = VEC && seg + S::kWaveElems <= n;
+    T e[S::kItems];
+    if (whole)
+        load_vec<T, VPT>(in, seg, lane, e);
+    else
+        load_scalar<T, VPT>(in, seg, n, lane, e, T(0));
+
+    T off[VPT];
+    T wave_excl;
+    const T agg = tile_local_scan<T, V, VPT>(e, off, wave_excl, s_wave);
+    const T prefix =
+        num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit) : T(0);
+    tile_finish<T, V, VPT, INCLUSIVE>(e, off, wave_excl, prefix);
+
+    if (whole)
+        store_vec<T, VPT>(out, seg, lane, e);
+    else
+        store_scalar<T, VPT>(out, seg, n, lane, e);
+}
+
+template <typename T, bool INCL, bool VEC>
+static hipError_t lookback_typed(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
+                                 hipStream_t st)
+{
+    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
+    lookback_scan_kernel<T, INCL, VEC, kVPT><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+        (const T*)in, (T*)out, n, tiles, ws.ctrl, ws.status, spin);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t lookback_dispatch(bool incl, const void* in, void* out, int64_t n, const DevWs& ws,
+                                    uint32_t spin, hipStream_t st)
+{
+    const bool vec = aligned16(in) && aligned16(out);
+    if (incl)
+        return vec ? lookback_typed<T, true, true>(in, out, n, ws, spin, st)
+                   : lookback_typed<T, true, false>(in, out, n, ws, spin, st);
+    return vec ? lookback_typed<T, false, true>(in, out, n, ws, spin, st)
+               : lookback_typed<T, false, false>(in, out, n, ws, spin, st);
+}
+
+hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
+                                const DevWs& ws, uint32_t spin_limit, hipStream_t stream)
+{
+    switch (kind) {
+    case kF32: return lookback_dispatch<float>(inclusive, in, out, n, ws, spin_limit, stream);
+    case kU64:
+    case kI64: return lookback_dispatch<uint64_t>(inclusive, in, out, n, ws, spin_limit, stream);
+    default: return lookback_dispatch<uint32_t>(inclusive, in, out, n, ws, spin_limit, stream);
+    }
+}
+
+}  // namespace ds

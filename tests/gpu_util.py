@@ -94,7 +94,7 @@ def gpu_compact(x: np.ndarray, op: str, operand, in_place: bool = False):
 
 
 SCAN_TILE_BYTES = 65536     # one scan workgroup's tile
-COMPACT_TILE_BYTES = 16384  # one compaction workgroup's tile
+COMPACT_TILE_BYTES = 65536  # one compaction workgroup's tile
 
 
 def tile_of(dtype, compact: bool = False) -> int:
