@@ -4,28 +4,22 @@
 // other parallel patterns", section "Stream compaction", first exercise,
 // fused form).
 #include "device_scan.hpp"
+#include "devscan.h"
 
 namespace ds {
 
-// The comparison as three compares and launch-uniform masks, no branch per
-// element: keep = (lt & m.lt) | (gt & m.gt) | (eq & m.eq) | (!eq & m.ne).
-// With lt = v < c, gt = c < v, eq = v == c this gives < <= > >= == != in the
-// element type's own order; a NaN has lt = gt = eq = false, so it is kept
-// only under !=.
-struct CmpMask {
-    bool lt, gt, eq, ne;
-};
-
-__host__ __device__ inline CmpMask cmp_mask(int cmp)
+// The comparison, fixed at compile time (one kernel per operator): a single
+// compare per element in the element type's own order. A NaN compares false
+// under every operator except !=.
+template <int CMP, typename T>
+__device__ __forceinline__ bool keep(T v, T c)
 {
-    return CmpMask{cmp == 0 || cmp == 1, cmp == 2 || cmp == 3, cmp == 1 || cmp == 3 || cmp == 4, cmp == 5};
-}
-
-template <typename T>
-__device__ __forceinline__ bool keep(T v, CmpMask m, T c)
-{
-    const bool lt = v < c, gt = c < v, eq = v == c;
-    return (lt && m.lt) || (gt && m.gt) || (eq && m.eq) || (!eq && m.ne);
+    if constexpr (CMP == DS_LT) return v < c;
+    if constexpr (CMP == DS_LE) return v <= c;
+    if constexpr (CMP == DS_GT) return v > c;
+    if constexpr (CMP == DS_GE) return v >= c;
+    if constexpr (CMP == DS_EQ) return v == c;
+    return v != c;
 }
 
 // Compaction over the scan's 64 KiB tiles. The keep flags live as one bit per
@@ -44,10 +38,10 @@ __device__ __forceinline__ void wave_lds_sync()
 
 constexpr int kGroup = 8;  // vector indices per staging round: 8 KiB of LDS per wave
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int CMP>
 __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* out, int64_t* num_selected,
-                                                               int64_t n, int64_t num_tiles, int cmp, T operand,
-                                                               Ctrl* ctrl, uint64_t* status, uint32_t spin_limit)
+                                                               int64_t n, int64_t num_tiles, T operand, Ctrl* ctrl,
+                                                               uint64_t* status, uint32_t spin_limit)
 {
     using S = Shape<T, kVPT>;
     constexpr int V = S::kPerVec;
@@ -69,14 +63,13 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
     else
         load_scalar<T, kVPT>(in, seg, n, lane, e, T(0));
 
-    const CmpMask m = cmp_mask(cmp);
     uint64_t keepm = 0;
 #pragma unroll
     for (int k = 0; k < kVPT; ++k)
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             const int i = k * V + j;
-            if ((whole || elem_index<T>(seg, k, j, lane) < n) && keep(e[i], m, operand)) keepm |= 1ull << i;
+            if ((whole || elem_index<T>(seg, k, j, lane) < n) && keep<CMP>(e[i], operand)) keepm |= 1ull << i;
         }
     uint32_t cnt[kVPT];
 #pragma unroll
@@ -132,23 +125,37 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
     if (tile == num_tiles - 1 && threadIdx.x == 0) *num_selected = (int64_t)prefix + agg;
 }
 
+template <typename T, int CMP>
+static hipError_t compact_cmp(const void* in, void* out, int64_t* num_selected, int64_t n, T operand,
+                              const DevWs& ws, uint32_t spin, hipStream_t st)
+{
+    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
+    if (aligned16(in) && aligned16(out))
+        compact_kernel<T, true, CMP><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+            (const T*)in, (T*)out, num_selected, n, tiles, operand, ws.ctrl, ws.status, spin);
+    else
+        compact_kernel<T, false, CMP><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+            (const T*)in, (T*)out, num_selected, n, tiles, operand, ws.ctrl, ws.status, spin);
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t compact_typed(const void* in, void* out, int64_t* num_selected, int64_t n, int cmp,
                                 uint64_t operand_bits, const DevWs& ws, uint32_t spin, hipStream_t st)
 {
-    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
     T operand;
     if constexpr (sizeof(T) == 4)
         operand = __builtin_bit_cast(T, (uint32_t)operand_bits);
     else
         operand = __builtin_bit_cast(T, operand_bits);
-    if (aligned16(in) && aligned16(out))
-        compact_kernel<T, true><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
-            (const T*)in, (T*)out, num_selected, n, tiles, cmp, operand, ws.ctrl, ws.status, spin);
-    else
-        compact_kernel<T, false><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
-            (const T*)in, (T*)out, num_selected, n, tiles, cmp, operand, ws.ctrl, ws.status, spin);
-    return hipGetLastError();
+    switch (cmp) {
+    case DS_LT: return compact_cmp<T, DS_LT>(in, out, num_selected, n, operand, ws, spin, st);
+    case DS_LE: return compact_cmp<T, DS_LE>(in, out, num_selected, n, operand, ws, spin, st);
+    case DS_GT: return compact_cmp<T, DS_GT>(in, out, num_selected, n, operand, ws, spin, st);
+    case DS_GE: return compact_cmp<T, DS_GE>(in, out, num_selected, n, operand, ws, spin, st);
+    case DS_EQ: return compact_cmp<T, DS_EQ>(in, out, num_selected, n, operand, ws, spin, st);
+    default: return compact_cmp<T, DS_NE>(in, out, num_selected, n, operand, ws, spin, st);
+    }
 }
 
 hipError_t launch_compact(ElemKind kind, const void* in, void* out, int64_t* num_selected, int64_t n, int cmp,
