@@ -74,6 +74,94 @@ def check_outputs(x_i, x_f, d_yi, d_yf) -> float:
     return ratio
 
 
+def tile_lds_experiment(args):
+    """The pages' block-scan table on MI355X: 4,096-element tiles scanned in LDS
+    by the work-efficient tree (unpadded, i + i/32, i + i/32 + i/1024) and by
+    the double-buffered Hillis-Steele scan, each timed alone and inside the
+    three-kernel pipeline, on 10,000,000 fp32 values that are 1.0 except every
+    fourth 2.0 (every prefix exact, so the pipeline is checked bit for bit
+    before it is timed). GB/s use the pages' 4 * n * 4 bytes for a pipeline."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import primitives_device_scan_amd as ds
+    from primitives_device_scan_amd import lds_model
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    L = ds.lib
+    n = 10_000_000
+    x = torch.from_numpy(datagen.quarter_twos_f32(n)).to(dev)
+    y = torch.empty_like(x)
+    sums = torch.empty((n + 4095) // 4096, dtype=torch.float32, device=dev)
+    i = np.arange(n, dtype=np.int64)
+    want = (i + i // 4).astype(np.float32)
+
+    def tile(v):
+        st = L.ds_tile_scan(ds.DS_FP32, v, x.data_ptr(), y.data_ptr(), sums.data_ptr(), n, sh)
+        if st:
+            raise ds.DevscanError(st, "ds_tile_scan")
+
+    def pipe(v):
+        st = L.ds_tile_pipeline(ds.DS_FP32, v, x.data_ptr(), y.data_ptr(), n, sh)
+        if st:
+            raise ds.DevscanError(st, "ds_tile_pipeline")
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in es:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in es]))
+
+    for name, v in ds.TILE_VARIANTS.items():
+        pipe(v)
+        torch.cuda.synchronize()
+        if not np.array_equal(y.cpu().numpy(), want):
+            log(f"pipeline {name} is not exact")
+            sys.exit(1)
+    if args.profile_only:
+        for v in ds.TILE_VARIANTS.values():
+            for _ in range(max(1, args.steps)):
+                tile(v)
+        # the other LDS users, once each: the look-back scan and compaction
+        xi = torch.from_numpy(datagen.workload("int32_100m", 10_000_000)).to(dev)
+        L.scan_exclusive(ds.DS_INT32, xi.data_ptr(), xi.data_ptr(), xi.numel(), sh)
+        cnt = torch.empty(1, dtype=torch.int64, device=dev)
+        L.compact_if(ds.DS_INT32, xi.data_ptr(), y.data_ptr(), cnt.data_ptr(), xi.numel(), ds.CMP[">"], 0, sh)
+        torch.cuda.synchronize()
+        log("profile run done")
+        return
+    copy_ms = timed(lambda: L.ds_copy(x.data_ptr(), y.data_ptr(), n * 4, sh))
+    copy_gbs = 2.0 * n * 4 / (copy_ms * 1e-3) / 1e9
+    rows = []
+    for name, v in ds.TILE_VARIANTS.items():
+        t_ms = timed(lambda: tile(v))
+        p_ms = timed(lambda: pipe(v))
+        gbs = 4.0 * n * 4 / (p_ms * 1e-3) / 1e9
+        row = {"variant": name, "tile_us": round(t_ms * 1e3, 1), "pipeline_us": round(p_ms * 1e3, 1),
+               "pipeline_gbs_4n": round(gbs, 1), "pct_of_copy_rate": round(100 * gbs / copy_gbs, 1)}
+        if name in lds_model.PADS:
+            row["model_requests_per_tile"] = lds_model.tree_requests(lds_model.PADS[name])
+            row["model_conflict_cycles_per_tile"] = lds_model.tree_conflict_cycles(pad=lds_model.PADS[name])
+        else:
+            row["model_requests_per_tile"] = lds_model.hs_requests()
+            row["model_conflict_cycles_per_tile"] = 0
+        rows.append(row)
+    lb_ms = timed(lambda: L.scan_exclusive(ds.DS_FP32, x.data_ptr(), y.data_ptr(), n, sh))
+    print(json.dumps({"mode": "tile_lds", "n": n, "dtype": "fp32", "tile": 4096, "threads": 1024,
+                      "copy_us": round(copy_ms * 1e3, 1), "copy_gbs": round(copy_gbs, 1), "rows": rows,
+                      "lookback_scan_us_same_input": round(lb_ms * 1e3, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +173,8 @@ def main():
     ap.add_argument("--profile-only", action="store_true",
                     help="inputs, one check, then --steps scans and --steps copies; no timing (for rocprofv3 runs)")
     ap.add_argument("--no-check", action="store_true", help="with --profile-only: skip the oracle check")
+    ap.add_argument("--tile-lds", action="store_true",
+                    help="the pages' LDS block-scan experiment instead of the main bench (own JSON line)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -92,6 +182,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the scan has no multi-GPU path in this library", file=sys.stderr)
         sys.exit(2)
+
+    if args.tile_lds:
+        return tile_lds_experiment(args)
 
     import numpy as np
     import torch

@@ -51,6 +51,14 @@ typedef enum {
     DS_ALGO_THREE_PASS = 2 /* three launches: reduce tiles, scan tile totals, rescan tiles seeded */
 } ds_algo;
 
+/* Block-level tile scan held in LDS, for ds_tile_scan / ds_tile_pipeline. */
+typedef enum {
+    DS_TILE_TREE = 0,      /* work-efficient up-sweep / down-sweep tree, word i at i */
+    DS_TILE_TREE_PAD1 = 1, /* same tree, word i at i + i/32 */
+    DS_TILE_TREE_PAD2 = 2, /* same tree, word i at i + i/32 + i/1024 */
+    DS_TILE_HS = 3         /* Hillis-Steele, double-buffered */
+} ds_tile_variant;
+
 typedef enum {
     DS_OK = 0,
     DS_ERR_INVALID_VALUE = 1,     /* n < 0, null pointer with n > 0, bad enum value */
@@ -128,6 +136,32 @@ int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected
  * and both pointers 16-byte aligned; the buffers must not overlap.
  */
 int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream);
+
+/*
+ * The pages' block-scan experiment on gfx950: each 4,096-element tile of d_in
+ * is scanned (exclusive) by one 1,024-thread workgroup in LDS with the given
+ * ds_tile_variant, and each tile's total goes to d_tile_sums (ceil(n/4096)
+ * elements, may be NULL). The tiles are independent: this is a block scan,
+ * not a device scan. "Day 32 -- The CUDA scan algorithm: the tree and the
+ * three kernels", sections "Two sweeps over one tree" and "The stride doubles,
+ * and so does the conflict"; "Day 31 -- CUDA prefix sum, the Hillis-Steele
+ * scan", section "Why one array is not enough".
+ *   dtype   DS_INT32, DS_UINT32 or DS_FP32 (DS_ERR_UNSUPPORTED_DTYPE otherwise)
+ *   d_out   n elements, may equal d_in, must not otherwise overlap it
+ *   n       0 <= n < 2^32
+ * Other arguments and errors as scan_exclusive.
+ */
+int ds_tile_scan(int dtype, int variant, const void* d_in, void* d_out, void* d_tile_sums, int64_t n,
+                 hipStream_t stream);
+
+/*
+ * The pages' three-kernel device scan built on ds_tile_scan: scan every tile
+ * and save its total, scan the totals (one workgroup, carried sum), add each
+ * tile's offset to every element of the tile. Exclusive; reads and writes the
+ * data twice ("Day 32", section "One block scans 4,096. Ten million needs
+ * three kernels."). Arguments and errors as ds_tile_scan, without d_tile_sums.
+ */
+int ds_tile_pipeline(int dtype, int variant, const void* d_in, void* d_out, int64_t n, hipStream_t stream);
 
 /*
  * Waits for `stream` and reports, in *timed_out, whether any look-back wait

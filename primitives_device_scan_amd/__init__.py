@@ -3,13 +3,15 @@ stream compaction for AMD Instinct MI355X (gfx950).
 
 The work runs in hand-written HIP kernels behind the C ABI of
 include/devscan.h (libdevscan.so, built in-tree by
-``python -m primitives_device_scan_amd.build``). This package is its Python
+``python primitives_device_scan_amd/build.py``). This package is its Python
 binding: argument checks and marshalling, with torch for device memory and
 streams. Importing it fails when the library is missing.
 """
 from ._binding import (ALGO, CMP, DS_FP32, DS_INT32, DS_INT64, DS_UINT32, DS_UINT64, EXPORTS, LIB_PATH,
-                       DevscanError, compact_if, copy, dtype_code, lib, load_library, operand_bits,
-                       query_timeout, release_workspace, scan, scan_exclusive, scan_inclusive, set_spin_limit)
+                       TILE_VARIANTS, DevscanError, compact_if, copy, dtype_code, lib, load_library, operand_bits,
+                       query_timeout, release_workspace, scan, scan_exclusive, scan_inclusive, set_spin_limit,
+                       tile_pipeline, tile_scan)
 
-__all__ = ["scan", "scan_exclusive", "scan_inclusive", "compact_if", "copy", "query_timeout", "set_spin_limit",
-           "release_workspace", "DevscanError", "lib", "LIB_PATH", "EXPORTS", "ALGO", "CMP"]
+__all__ = ["scan", "scan_exclusive", "scan_inclusive", "compact_if", "copy", "tile_scan", "tile_pipeline",
+           "query_timeout", "set_spin_limit", "release_workspace", "DevscanError", "lib", "LIB_PATH", "EXPORTS",
+           "ALGO", "CMP", "TILE_VARIANTS"]

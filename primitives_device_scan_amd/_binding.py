@@ -21,13 +21,14 @@ CMP = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
 ALGO = {"default": 0, "lookback": 1, "three_pass": 2}
 DS_OK = 0
 
-EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_copy", "ds_query_timeout",
-           "ds_set_spin_limit", "ds_status_string", "ds_release_workspace", "ds_version"]
+EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
+           "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace", "ds_version"]
+TILE_VARIANTS = {"tree": 0, "tree_pad1": 1, "tree_pad2": 2, "hillis_steele": 3}
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with `python -m primitives_device_scan_amd.build` "
+        raise ImportError(f"{path} is missing: build it with `python primitives_device_scan_amd/build.py` "
                           "(or __graft_entry__.build()); there is no CPU fallback")
     L = ctypes.CDLL(path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -40,6 +41,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.compact_if.restype = I
     L.ds_copy.argtypes = [P, P, I64, P]
     L.ds_copy.restype = I
+    L.ds_tile_scan.argtypes = [I, I, P, P, P, I64, P]
+    L.ds_tile_scan.restype = I
+    L.ds_tile_pipeline.argtypes = [I, I, P, P, I64, P]
+    L.ds_tile_pipeline.restype = I
     L.ds_query_timeout.argtypes = [P, ctypes.POINTER(I)]
     L.ds_query_timeout.restype = I
     L.ds_set_spin_limit.argtypes = [ctypes.c_uint32]
@@ -180,6 +185,38 @@ def copy(src: torch.Tensor, dst: torch.Tensor, *, stream=None) -> torch.Tensor:
     with torch.cuda.device(src.device):
         _check(lib.ds_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(src, stream)), "ds_copy")
     return dst
+
+
+def tile_scan(x: torch.Tensor, variant: str, out: torch.Tensor | None = None,
+              tile_sums: torch.Tensor | None = None, *, stream=None):
+    """Block-level exclusive scan of every 4,096-element tile of x in LDS; returns (out, tile_sums)."""
+    _check_tensor(x, "x")
+    code = dtype_code(x.dtype)
+    out = torch.empty_like(x) if out is None else out
+    tiles = (x.numel() + 4095) // 4096
+    tile_sums = torch.empty(tiles, dtype=x.dtype, device=x.device) if tile_sums is None else tile_sums
+    _check_tensor(out, "out")
+    _check_tensor(tile_sums, "tile_sums")
+    if tile_sums.numel() < tiles or tile_sums.dtype != x.dtype or out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x; tile_sums must hold ceil(n/4096) elements of x's dtype")
+    with torch.cuda.device(x.device):
+        _check(lib.ds_tile_scan(code, TILE_VARIANTS[variant], x.data_ptr(), out.data_ptr(), tile_sums.data_ptr(),
+                                x.numel(), _stream_handle(x, stream)), "ds_tile_scan")
+    return out, tile_sums
+
+
+def tile_pipeline(x: torch.Tensor, variant: str, out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
+    """Device-wide exclusive scan by the three-kernel pipeline over LDS tile scans."""
+    _check_tensor(x, "x")
+    code = dtype_code(x.dtype)
+    out = torch.empty_like(x) if out is None else out
+    _check_tensor(out, "out")
+    if out.numel() != x.numel() or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    with torch.cuda.device(x.device):
+        _check(lib.ds_tile_pipeline(code, TILE_VARIANTS[variant], x.data_ptr(), out.data_ptr(), x.numel(),
+                                    _stream_handle(x, stream)), "ds_tile_pipeline")
+    return out
 
 
 def query_timeout(device=None, stream=None) -> bool:

@@ -1,6 +1,8 @@
 """Builds libdevscan.so (the HIP library behind include/devscan.h) in-tree.
 
-    python -m primitives_device_scan_amd.build
+    python primitives_device_scan_amd/build.py
+
+(Run it as a script, not with -m: importing the package loads the library.)
 
 Compiles every HIP source for gfx950 with hipcc. Packed fp32 instructions are
 disabled for the device code (-target-feature -packed-fp32-ops).
@@ -16,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdevscan.so")
-SOURCES = ["scan_lookback.hip", "scan_three_pass.hip", "compact.hip", "copy.hip", "api.hip"]
+SOURCES = ["scan_lookback.hip", "scan_three_pass.hip", "compact.hip", "copy.hip", "tile_lds.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

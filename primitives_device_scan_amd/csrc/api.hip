@@ -203,6 +203,40 @@ int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream)
     return ds::launch_copy(d_in, d_out, nbytes, stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
+static int check_tile_args(int dtype, int variant, const void* in, void* out, int64_t n)
+{
+    if (!valid_dtype(dtype)) return DS_ERR_UNSUPPORTED_DTYPE;
+    if (elem_bytes(dtype) != 4) return DS_ERR_UNSUPPORTED_DTYPE;
+    if (variant < DS_TILE_TREE || variant > DS_TILE_HS) return DS_ERR_INVALID_VALUE;
+    if (n >= ((int64_t)1 << 32)) return DS_ERR_TOO_LARGE;
+    return check_io(dtype, in, out, n, true);
+}
+
+int ds_tile_scan(int dtype, int variant, const void* d_in, void* d_out, void* d_tile_sums, int64_t n,
+                 hipStream_t stream)
+{
+    int st = check_tile_args(dtype, variant, d_in, d_out, n);
+    if (st != DS_OK || n == 0) return st;
+    if (((uintptr_t)d_tile_sums) % 4) return DS_ERR_MISALIGNED;
+    return ds::launch_tile_scan(kind_of(dtype), variant, d_in, d_out, d_tile_sums, n, stream) == hipSuccess
+               ? DS_OK
+               : DS_ERR_HIP;
+}
+
+int ds_tile_pipeline(int dtype, int variant, const void* d_in, void* d_out, int64_t n, hipStream_t stream)
+{
+    int st = check_tile_args(dtype, variant, d_in, d_out, n);
+    if (st != DS_OK || n == 0) return st;
+    const int64_t tiles = (n + ds::lds_tile_elems() - 1) / ds::lds_tile_elems();
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace* w = nullptr;
+    st = get_workspace(stream, tiles, &w);
+    if (st != DS_OK) return st;
+    return ds::launch_tile_pipeline(kind_of(dtype), variant, d_in, d_out, n, view(*w), stream) == hipSuccess
+               ? DS_OK
+               : DS_ERR_HIP;
+}
+
 int ds_query_timeout(hipStream_t stream, int* timed_out)
 {
     if (!timed_out) return DS_ERR_INVALID_VALUE;

@@ -34,4 +34,14 @@ hipError_t launch_compact(ElemKind kind, const void* in, void* out, int64_t* num
 
 hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t stream);
 
+// Exclusive scan of `count` tile totals in place (one workgroup, carried sum).
+hipError_t launch_scan_totals(ElemKind kind, void* totals, int64_t count, hipStream_t stream);
+
+// 4,096-element tile scans in LDS and the three-kernel pipeline built on them.
+int64_t lds_tile_elems();
+hipError_t launch_tile_scan(ElemKind kind, int variant, const void* in, void* out, void* tile_sums, int64_t n,
+                            hipStream_t stream);
+hipError_t launch_tile_pipeline(ElemKind kind, int variant, const void* in, void* out, int64_t n,
+                                const DevWs& ws, hipStream_t stream);
+
 }  // namespace ds

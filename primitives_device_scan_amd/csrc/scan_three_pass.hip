@@ -133,4 +133,16 @@ hipError_t launch_three_pass_scan(ElemKind kind, bool inclusive, const void* in,
     }
 }
 
+hipError_t launch_scan_totals(ElemKind kind, void* totals, int64_t count, hipStream_t stream)
+{
+    const dim3 grid(1), block(kTotalsThreads);
+    switch (kind) {
+    case kF32: scan_totals_kernel<float><<<grid, block, 0, stream>>>((float*)totals, count); break;
+    case kU64:
+    case kI64: scan_totals_kernel<uint64_t><<<grid, block, 0, stream>>>((uint64_t*)totals, count); break;
+    default: scan_totals_kernel<uint32_t><<<grid, block, 0, stream>>>((uint32_t*)totals, count); break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace ds

@@ -25,8 +25,8 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        import primitives_device_scan_amd.build as b
-        b.build()
+        import __graft_entry__
+        __graft_entry__.build()
     from primitives_device_scan_amd import _binding
     return _binding.load_library(LIB)
 
