@@ -81,9 +81,9 @@ typedef enum {
  *   d_in    device pointer to n elements (read)
  *   d_out   device pointer to n elements (written); may equal d_in (in place),
  *           must not otherwise overlap it
- *   n       element count, n >= 0; n == 0 enqueues nothing. At most 2^24 - 1
- *           tiles of 64 KiB: 274,877,890,560 four-byte or 137,438,945,280
- *           eight-byte elements (DS_ERR_TOO_LARGE beyond)
+ *   n       element count, n >= 0; n == 0 enqueues nothing; n <= 68,719,472,640
+ *           (2^24 - 1 blocks of 4,096: the grid of any entry point stays below
+ *           2^32 work-items), DS_ERR_TOO_LARGE beyond
  *   stream  HIP stream of the current device (0 = null stream)
  * Returns DS_OK or a ds_status error.
  */
@@ -177,6 +177,22 @@ int ds_query_timeout(hipStream_t stream, int* timed_out);
  * process. Small values exist to test the give-up path.
  */
 int ds_set_spin_limit(uint32_t polls);
+
+/* Which entry point's tile ds_tile_elems reports. */
+typedef enum {
+    DS_TILE_OF_SCAN_EXCLUSIVE = 0, /* scan_exclusive, ds_scan look-back exclusive */
+    DS_TILE_OF_SCAN_INCLUSIVE = 1, /* scan_inclusive, ds_scan look-back inclusive */
+    DS_TILE_OF_THREE_PASS = 2,     /* DS_ALGO_THREE_PASS */
+    DS_TILE_OF_COMPACT = 3,        /* compact_if */
+    DS_TILE_OF_LDS_TILE_SCAN = 4   /* ds_tile_scan / ds_tile_pipeline (4-byte types only) */
+} ds_tile_of;
+
+/*
+ * Elements of `dtype` one workgroup of the given entry point (ds_tile_of)
+ * handles: the granularity of its tiles, for callers that size work or
+ * tests that aim at tile boundaries. Returns -1 for an invalid dtype or entry.
+ */
+int64_t ds_tile_elems(int dtype, int entry);
 
 /* Human-readable name of a ds_status value (static storage). */
 const char* ds_status_string(int status);

@@ -22,7 +22,9 @@ ALGO = {"default": 0, "lookback": 1, "three_pass": 2}
 DS_OK = 0
 
 EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
-           "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace", "ds_version"]
+           "ds_tile_elems", "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace",
+           "ds_version"]
+TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4}
 TILE_VARIANTS = {"tree": 0, "tree_pad1": 1, "tree_pad2": 2, "hillis_steele": 3}
 
 
@@ -53,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ds_status_string.restype = ctypes.c_char_p
     L.ds_release_workspace.argtypes = []
     L.ds_release_workspace.restype = None
+    L.ds_tile_elems.argtypes = [I, I]
+    L.ds_tile_elems.restype = I64
     L.ds_version.argtypes = []
     L.ds_version.restype = I
     return L

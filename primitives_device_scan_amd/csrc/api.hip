@@ -105,8 +105,8 @@ int check_io(int dtype, const void* in, const void* out, int64_t n, bool allow_s
     if (n == 0) return DS_OK;
     if (!in || !out) return DS_ERR_INVALID_VALUE;
     const int64_t sz = elem_bytes(dtype);
-    const int64_t tiles = (n + ds::tile_elems(sz) - 1) / ds::tile_elems(sz);
-    if (tiles > kMaxTiles) return DS_ERR_TOO_LARGE;
+    const int64_t smallest_tile = ds::lds_tile_elems();  // 4,096: the most tiles any entry point launches
+    if ((n + smallest_tile - 1) / smallest_tile > kMaxTiles) return DS_ERR_TOO_LARGE;
     if (((uintptr_t)in % sz) || ((uintptr_t)out % sz)) return DS_ERR_MISALIGNED;
     const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out, len = (uintptr_t)(n * sz);
     if (a == b) return allow_same ? DS_OK : DS_ERR_OVERLAP;
@@ -120,7 +120,13 @@ int scan_impl(int dtype, int inclusive, int algo, const void* in, void* out, int
     if (algo < DS_ALGO_DEFAULT || algo > DS_ALGO_THREE_PASS) return DS_ERR_INVALID_VALUE;
     int st = check_io(dtype, in, out, n, true);
     if (st != DS_OK || n == 0) return st;
-    const int64_t tiles = (n + ds::tile_elems(elem_bytes(dtype)) - 1) / ds::tile_elems(elem_bytes(dtype));
+    // Choose the kernel first, then size the workspace by that kernel's own
+    // tiles: the look-back and three-pass tiles differ in size, and a
+    // three-pass call on one tile runs the look-back kernel instead.
+    const int64_t tp = ds::three_pass_tile_elems(elem_bytes(dtype));
+    const bool three = algo == DS_ALGO_THREE_PASS && n > tp;
+    const int64_t te = three ? tp : ds::tile_elems(kind_of(dtype), inclusive != 0);
+    const int64_t tiles = (n + te - 1) / te;
     std::lock_guard<std::mutex> lock(g_mu);
     DevWs dws{nullptr, nullptr, nullptr};
     Workspace* w = nullptr;
@@ -130,7 +136,7 @@ int scan_impl(int dtype, int inclusive, int algo, const void* in, void* out, int
         dws = view(*w);
     }
     hipError_t e;
-    if (algo == DS_ALGO_THREE_PASS && tiles > 1) {
+    if (three) {
         e = ds::launch_three_pass_scan(kind_of(dtype), inclusive != 0, in, out, n, dws, stream);
     } else {
         e = ds::launch_lookback_scan(kind_of(dtype), inclusive != 0, in, out, n, dws, g_spin_limit, stream);
@@ -287,6 +293,20 @@ void ds_release_workspace(void)
     for (auto& kv : g_ws)
         if (kv.second.base) (void)hipFree(kv.second.base);
     g_ws.clear();
+}
+
+int64_t ds_tile_elems(int dtype, int entry)
+{
+    if (!valid_dtype(dtype)) return -1;
+    const int b = elem_bytes(dtype);
+    switch (entry) {
+    case DS_TILE_OF_SCAN_EXCLUSIVE: return ds::tile_elems(kind_of(dtype), false);
+    case DS_TILE_OF_SCAN_INCLUSIVE: return ds::tile_elems(kind_of(dtype), true);
+    case DS_TILE_OF_THREE_PASS: return ds::three_pass_tile_elems(b);
+    case DS_TILE_OF_COMPACT: return ds::compact_tile_elems(b);
+    case DS_TILE_OF_LDS_TILE_SCAN: return b == 4 ? ds::lds_tile_elems() : -1;
+    default: return -1;
+    }
 }
 
 int ds_version(void) { return 1; }

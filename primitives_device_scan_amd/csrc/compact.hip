@@ -43,11 +43,11 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
                                                                int64_t n, int64_t num_tiles, T operand, Ctrl* ctrl,
                                                                uint64_t* status, uint32_t spin_limit)
 {
-    using S = Shape<T, kVPT>;
+    using S = Shape<T, kCompactVPT>;
     constexpr int V = S::kPerVec;
     constexpr int kBuf = kWave * V * kGroup + V;  // a round's slices plus the alignment shift
     static_assert(S::kItems <= 64, "keep mask is 64 bits");
-    static_assert(kVPT % kGroup == 0, "whole rounds");
+    static_assert(kCompactVPT % kGroup == 0, "whole rounds");
     __shared__ uint32_t s_wave[kWaves];
     __shared__ __attribute__((aligned(16))) T s_stage[kWaves][kBuf];
     const int lane = lane_id();
@@ -59,25 +59,25 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
     const bool whole = VEC && seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T, kVPT>(in, seg, lane, e);
+        load_vec<T, kCompactVPT>(in, seg, lane, e);
     else
-        load_scalar<T, kVPT>(in, seg, n, lane, e, T(0));
+        load_scalar<T, kCompactVPT>(in, seg, n, lane, e, T(0));
 
     uint64_t keepm = 0;
 #pragma unroll
-    for (int k = 0; k < kVPT; ++k)
+    for (int k = 0; k < kCompactVPT; ++k)
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             const int i = k * V + j;
             if ((whole || elem_index<T>(seg, k, j, lane) < n) && keep<CMP>(e[i], operand)) keepm |= 1ull << i;
         }
-    uint32_t cnt[kVPT];
+    uint32_t cnt[kCompactVPT];
 #pragma unroll
-    for (int k = 0; k < kVPT; ++k)
+    for (int k = 0; k < kCompactVPT; ++k)
         cnt[k] = (uint32_t)__builtin_popcountll((keepm >> (k * V)) & ((1ull << V) - 1));
-    uint32_t off[kVPT];
+    uint32_t off[kCompactVPT];
     uint32_t wave_excl;
-    const uint32_t agg = tile_local_scan<uint32_t, 1, kVPT>(cnt, off, wave_excl, s_wave);
+    const uint32_t agg = tile_local_scan<uint32_t, 1, kCompactVPT>(cnt, off, wave_excl, s_wave);
     const uint32_t wave_total = s_wave[wave];
 
     uint32_t prefix = 0;
@@ -90,9 +90,9 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
     const int64_t wave_base = (int64_t)prefix + wave_excl;  // output index of this wave's first kept element
     T* const stage = s_stage[wave];
 #pragma unroll
-    for (int g = 0; g < kVPT; g += kGroup) {
+    for (int g = 0; g < kCompactVPT; g += kGroup) {
         const uint32_t start = readlane(off[g], 0);  // rank of the round's first kept element in the wave
-        const uint32_t end = g + kGroup < kVPT ? readlane(off[g + kGroup], 0) : wave_total;
+        const uint32_t end = g + kGroup < kCompactVPT ? readlane(off[g + kGroup], 0) : wave_total;
         const int64_t first = wave_base + start;
         const uint32_t shift = VEC ? (uint32_t)(first % V) : 0u;
 #pragma unroll
@@ -129,7 +129,8 @@ template <typename T, int CMP>
 static hipError_t compact_cmp(const void* in, void* out, int64_t* num_selected, int64_t n, T operand,
                               const DevWs& ws, uint32_t spin, hipStream_t st)
 {
-    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
+    const int64_t tiles = (n + Shape<T, kCompactVPT>::kTile - 1) / Shape<T, kCompactVPT>::kTile;
+    if (tiles > 1 && (!ws.ctrl || !ws.status)) return hipErrorInvalidValue;  // several tiles need a workspace
     if (aligned16(in) && aligned16(out))
         compact_kernel<T, true, CMP><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
             (const T*)in, (T*)out, num_selected, n, tiles, operand, ws.ctrl, ws.status, spin);

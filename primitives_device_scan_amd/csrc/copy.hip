@@ -29,8 +29,8 @@ hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t st
     return hipGetLastError();
 }
 
-int64_t tile_elems(int elem_bytes) { return (int64_t)kTileBytes / elem_bytes; }
 int64_t tile_bytes() { return kTileBytes; }
+int64_t three_pass_tile_elems(int elem_bytes) { return (int64_t)kThreads * kThreePassVPT * kVecBytes / elem_bytes; }
 int64_t compact_tile_elems(int elem_bytes) { return (int64_t)kThreads * kCompactVPT * kVecBytes / elem_bytes; }
 
 }  // namespace ds

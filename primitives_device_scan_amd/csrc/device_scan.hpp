@@ -8,13 +8,23 @@
 
 namespace ds {
 
-// 16-byte vectors per thread: a tile is 256 threads x 16 x 16 B = 64 KiB
-// (16,384 four-byte or 8,192 eight-byte elements), for the scans and for
-// compaction. Large tiles keep enough bytes resident per CU for the look-back
-// latency (several microseconds under full HBM load) to hide behind other
-// tiles' transfers.
-constexpr int kVPT = 16;
-constexpr int kCompactVPT = kVPT;
+// 16-byte vectors per thread (VPT); a tile is 256 threads x VPT x 16 B.
+//  - look-back scan: the largest tile that fits 4 waves per SIMD without
+//    spilling (ScanVPT below), since resident tile bytes per CU are what hide
+//    the look-back latency (several microseconds under full HBM load) behind
+//    other tiles' transfers: 96 KiB for int32 exclusive, less where the
+//    arithmetic needs more registers (fp32, inclusive, 8-byte);
+//  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
+//    wait to hide; compaction's keep mask holds 64 elements).
+template <typename T, bool INCLUSIVE>
+struct ScanVPT {
+    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 12 : 16)
+                               : __is_same(T, float) ? (INCLUSIVE ? 16 : 20)
+                                                     : (INCLUSIVE ? 20 : 24);
+};
+constexpr int kVPT = 24;  // largest scan tile: the same-pattern copy uses it
+constexpr int kThreePassVPT = 16;
+constexpr int kCompactVPT = 16;
 constexpr int kTileBytes = kThreads * kVPT * kVecBytes;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

@@ -18,8 +18,9 @@ struct DevWs {
 
 enum ElemKind { kU32 = 0, kF32 = 1, kU64 = 2, kI32 = 3, kI64 = 4 };
 
-int64_t tile_elems(int elem_bytes);          // scan tile
-int64_t compact_tile_elems(int elem_bytes);  // compaction tile
+int64_t tile_elems(ElemKind kind, bool inclusive);  // look-back scan tile
+int64_t three_pass_tile_elems(int elem_bytes);  // three-pass scan tile
+int64_t compact_tile_elems(int elem_bytes);     // compaction tile
 int64_t tile_bytes();
 
 hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,

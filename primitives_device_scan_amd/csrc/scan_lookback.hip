@@ -8,7 +8,7 @@
 namespace ds {
 
 template <typename T, bool INCLUSIVE, bool VEC, int VPT>
-__global__ __launch_bounds__(kThreads) void lookback_scan_kernel(const T* in, T* out, int64_t n,
+__global__ __launch_bounds__(kThreads, 4) void lookback_scan_kernel(const T* in, T* out, int64_t n,
                                                                   int64_t num_tiles, Ctrl* ctrl,
                                                                   uint64_t* status, uint32_t spin_limit)
 {
@@ -30,12 +30,11 @@ __global__ __launch_bounds__(kThreads) void lookback_scan_kernel(const T* in, T*
     else
         load_scalar<T, VPT>(in, seg, n, lane, e, T(0));
 
-    T off[VPT];
     T wave_excl;
-    const T agg = tile_local_scan<T, V, VPT>(e, off, wave_excl, s_wave);
+    const T agg = tile_scan_in_wave<T, V, VPT, INCLUSIVE>(e, wave_excl, s_wave);
     const T prefix =
         num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit) : T(0);
-    tile_finish<T, V, VPT, INCLUSIVE>(e, off, wave_excl, prefix);
+    add_uniform(e, prefix + wave_excl);
 
     if (whole)
         store_vec<T, VPT>(out, seg, lane, e);
@@ -47,8 +46,10 @@ template <typename T, bool INCL, bool VEC>
 static hipError_t lookback_typed(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
                                  hipStream_t st)
 {
-    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
-    lookback_scan_kernel<T, INCL, VEC, kVPT><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+    constexpr int VPT = ScanVPT<T, INCL>::value;
+    const int64_t tiles = (n + Shape<T, VPT>::kTile - 1) / Shape<T, VPT>::kTile;
+    if (tiles > 1 && (!ws.ctrl || !ws.status)) return hipErrorInvalidValue;  // several tiles need a workspace
+    lookback_scan_kernel<T, INCL, VEC, VPT><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
         (const T*)in, (T*)out, n, tiles, ws.ctrl, ws.status, spin);
     return hipGetLastError();
 }
@@ -73,6 +74,19 @@ hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, v
     case kU64:
     case kI64: return lookback_dispatch<uint64_t>(inclusive, in, out, n, ws, spin_limit, stream);
     default: return lookback_dispatch<uint32_t>(inclusive, in, out, n, ws, spin_limit, stream);
+    }
+}
+
+int64_t tile_elems(ElemKind kind, bool inclusive)
+{
+    switch (kind) {
+    case kF32: return inclusive ? Shape<float, ScanVPT<float, true>::value>::kTile
+                                : Shape<float, ScanVPT<float, false>::value>::kTile;
+    case kU64:
+    case kI64: return inclusive ? Shape<uint64_t, ScanVPT<uint64_t, true>::value>::kTile
+                                : Shape<uint64_t, ScanVPT<uint64_t, false>::value>::kTile;
+    default: return inclusive ? Shape<uint32_t, ScanVPT<uint32_t, true>::value>::kTile
+                              : Shape<uint32_t, ScanVPT<uint32_t, false>::value>::kTile;
     }
 }
 

@@ -10,7 +10,7 @@ namespace ds {
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void tile_reduce_kernel(const T* in, int64_t n, T* totals)
 {
-    using S = Shape<T, kVPT>;
+    using S = Shape<T, kThreePassVPT>;
     __shared__ T s_wave[kWaves];
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
@@ -18,9 +18,9 @@ __global__ __launch_bounds__(kThreads) void tile_reduce_kernel(const T* in, int6
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
     T e[S::kItems];
     if (VEC && seg + S::kWaveElems <= n)
-        load_vec<T, kVPT>(in, seg, lane, e);
+        load_vec<T, kThreePassVPT>(in, seg, lane, e);
     else
-        load_scalar<T, kVPT>(in, seg, n, lane, e, T(0));
+        load_scalar<T, kThreePassVPT>(in, seg, n, lane, e, T(0));
     T s = T(0);
 #pragma unroll
     for (int i = 0; i < S::kItems; ++i) s = s + e[i];
@@ -70,7 +70,7 @@ template <typename T, bool INCLUSIVE, bool VEC>
 __global__ __launch_bounds__(kThreads) void tile_rescan_kernel(const T* in, T* out, int64_t n,
                                                                 const T* offsets)
 {
-    using S = Shape<T, kVPT>;
+    using S = Shape<T, kThreePassVPT>;
     constexpr int V = S::kPerVec;
     __shared__ T s_wave[kWaves];
     const int lane = lane_id();
@@ -80,24 +80,25 @@ __global__ __launch_bounds__(kThreads) void tile_rescan_kernel(const T* in, T* o
     const bool whole = VEC && seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T, kVPT>(in, seg, lane, e);
+        load_vec<T, kThreePassVPT>(in, seg, lane, e);
     else
-        load_scalar<T, kVPT>(in, seg, n, lane, e, T(0));
-    T off[kVPT];
+        load_scalar<T, kThreePassVPT>(in, seg, n, lane, e, T(0));
+    T off[kThreePassVPT];
     T wave_excl;
-    tile_local_scan<T, V, kVPT>(e, off, wave_excl, s_wave);
-    tile_finish<T, V, kVPT, INCLUSIVE>(e, off, wave_excl, offsets[tile]);
+    tile_local_scan<T, V, kThreePassVPT>(e, off, wave_excl, s_wave);
+    tile_finish<T, V, kThreePassVPT, INCLUSIVE>(e, off, wave_excl, offsets[tile]);
     if (whole)
-        store_vec<T, kVPT>(out, seg, lane, e);
+        store_vec<T, kThreePassVPT>(out, seg, lane, e);
     else
-        store_scalar<T, kVPT>(out, seg, n, lane, e);
+        store_scalar<T, kThreePassVPT>(out, seg, n, lane, e);
 }
 
 template <typename T, bool VEC>
 static hipError_t three_pass_typed(bool incl, const void* in, void* out, int64_t n, const DevWs& ws,
                                    hipStream_t st)
 {
-    const int64_t tiles = (n + Shape<T, kVPT>::kTile - 1) / Shape<T, kVPT>::kTile;
+    const int64_t tiles = (n + Shape<T, kThreePassVPT>::kTile - 1) / Shape<T, kThreePassVPT>::kTile;
+    if (!ws.totals) return hipErrorInvalidValue;
     T* totals = (T*)ws.totals;
     tile_reduce_kernel<T, VEC><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>((const T*)in, n, totals);
     hipError_t e = hipGetLastError();
@@ -135,6 +136,7 @@ hipError_t launch_three_pass_scan(ElemKind kind, bool inclusive, const void* in,
 
 hipError_t launch_scan_totals(ElemKind kind, void* totals, int64_t count, hipStream_t stream)
 {
+    if (!totals) return hipErrorInvalidValue;
     const dim3 grid(1), block(kTotalsThreads);
     switch (kind) {
     case kF32: scan_totals_kernel<float><<<grid, block, 0, stream>>>((float*)totals, count); break;

@@ -210,25 +210,88 @@ __device__ __forceinline__ T tile_local_scan(T (&e)[V * VPT], T (&off)[VPT], T& 
     return agg;
 }
 
+// tile_local_scan and fold_wave_offsets in one pass over the vectors: each
+// vector's wave scan is folded into its elements as soon as it is known, so
+// only the data and a few temporaries are live (the separate form keeps every
+// vector's scan and offset live at once). Out: e = each element's inclusive
+// or exclusive sum within its wave's segment, wave_excl = sum of the waves
+// before this one; returns the tile aggregate. One workgroup barrier.
+template <typename T, int V, int VPT, bool INCLUSIVE>
+__device__ __forceinline__ T tile_scan_in_wave(T (&e)[V * VPT], T& wave_excl, T* s_wave)
+{
+    const int lane = lane_id();
+    const int wave = (int)(threadIdx.x / kWave);
+    T run = T(0);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+#pragma unroll
+        for (int j = 1; j < V; ++j)
+            e[k * V + j] = e[k * V + j] + e[k * V + j - 1];
+        const T incl = wave_inclusive_scan(e[k * V + V - 1]);
+        const T off = run + wave_shift_right1(incl);
+        run = run + readlane(incl, kWave - 1);
+        if constexpr (INCLUSIVE) {
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                e[k * V + j] = off + e[k * V + j];
+        } else {
+#pragma unroll
+            for (int j = V - 1; j > 0; --j)
+                e[k * V + j] = off + e[k * V + j - 1];
+            e[k * V] = off;
+        }
+    }
+    if (lane == 0) s_wave[wave] = run;
+    __syncthreads();
+    T agg = T(0), before = T(0);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const T v = s_wave[w];
+        if (w < wave) before = before + v;
+        agg = agg + v;
+    }
+    wave_excl = before;
+    return agg;
+}
+
+// Folds the per-vector offsets into the values: e becomes each element's
+// inclusive or exclusive sum within its wave's segment, and `off` is no
+// longer needed (so it holds no registers while the tile waits for its
+// prefix).
+template <typename T, int V, int VPT, bool INCLUSIVE>
+__device__ __forceinline__ void fold_wave_offsets(T (&e)[V * VPT], const T (&off)[VPT])
+{
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        if constexpr (INCLUSIVE) {
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                e[k * V + j] = off[k] + e[k * V + j];
+        } else {
+#pragma unroll
+            for (int j = V - 1; j > 0; --j)
+                e[k * V + j] = off[k] + e[k * V + j - 1];
+            e[k * V] = off[k];
+        }
+    }
+}
+
+// Adds the same value (the tile's exclusive prefix plus the waves before this
+// one) to every element.
+template <typename T, int N>
+__device__ __forceinline__ void add_uniform(T (&e)[N], T head)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        e[i] = head + e[i];
+}
+
 // Final values from the local scan and the tile's exclusive prefix.
 template <typename T, int V, int VPT, bool INCLUSIVE>
 __device__ __forceinline__ void tile_finish(T (&e)[V * VPT], const T (&off)[VPT], T wave_excl, T prefix)
 {
-    const T head = prefix + wave_excl;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const T base = head + off[k];
-        if constexpr (INCLUSIVE) {
-#pragma unroll
-            for (int j = 0; j < V; ++j)
-                e[k * V + j] = base + e[k * V + j];
-        } else {
-#pragma unroll
-            for (int j = V - 1; j > 0; --j)
-                e[k * V + j] = base + e[k * V + j - 1];
-            e[k * V] = base;
-        }
-    }
+    fold_wave_offsets<T, V, VPT, INCLUSIVE>(e, off);
+    add_uniform(e, prefix + wave_excl);
 }
 
 // ---------------------------------------------------------------------------

@@ -164,6 +164,7 @@ hipError_t launch_tile_pipeline(ElemKind kind, int variant, const void* in, void
                                 const DevWs& ws, hipStream_t stream)
 {
     const int64_t tiles = (n + kLdsTile - 1) / kLdsTile;
+    if (!ws.totals) return hipErrorInvalidValue;
     hipError_t e = launch_tile_scan(kind, variant, in, out, ws.totals, n, stream);
     if (e != hipSuccess) return e;
     e = launch_scan_totals(kind, ws.totals, tiles, stream);

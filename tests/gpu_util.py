@@ -93,12 +93,13 @@ def gpu_compact(x: np.ndarray, op: str, operand, in_place: bool = False):
     return from_dev(out, x.dtype, 0, n), k
 
 
-SCAN_TILE_BYTES = 65536     # one scan workgroup's tile
-COMPACT_TILE_BYTES = 65536  # one compaction workgroup's tile
-
-
-def tile_of(dtype, compact: bool = False) -> int:
-    return (COMPACT_TILE_BYTES if compact else SCAN_TILE_BYTES) // np.dtype(dtype).itemsize
+def tile_of(dtype, compact: bool = False, entry: str | None = None) -> int:
+    """Elements per workgroup tile, as the library reports it (ds_tile_elems);
+    by default the smaller of the exclusive and inclusive scan tiles."""
+    if entry is None and not compact:
+        return min(tile_of(dtype, entry="scan_exclusive"), tile_of(dtype, entry="scan_inclusive"))
+    entry = entry or "compact"
+    return int(ds.lib.ds_tile_elems(CODE[np.dtype(dtype)], ds._binding.TILE_OF[entry]))
 
 
 def assert_int_equal(got: np.ndarray, want: np.ndarray, what: str):

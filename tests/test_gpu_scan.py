@@ -215,3 +215,19 @@ def test_give_up_path_then_recovery():
     for _ in range(3):
         check_scan(x, False, gpu_scan(x, False), "after give-up")
     assert ds.query_timeout() is False
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+def test_three_pass_on_one_tile_runs_the_lookback_kernel(dt):
+    """Sizes around both tile sizes: a three-pass call whose input fits one
+    three-pass tile runs the look-back kernel, whose tiles can be smaller
+    (a regression test for a workspace that was sized by the wrong tile)."""
+    sizes = set()
+    for entry in ("scan_exclusive", "scan_inclusive", "three_pass"):
+        t = tile_of(dt, entry=entry)
+        sizes |= {t - 1, t, t + 1, 2 * t - 1, 2 * t + 1}
+    for n in sorted(sizes):
+        x = _input(dt, n, 5000 + n)
+        for inc in (False, True):
+            check_scan(x, inc, gpu_scan(x, inc, "three_pass"), f"three_pass n={n} inc={inc}")
+            check_scan(x, inc, gpu_scan(x, inc, "lookback"), f"lookback n={n} inc={inc}")
