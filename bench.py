@@ -321,6 +321,13 @@ def main():
         extras["compact_256m_us"] = round(c_ms * 1e3, 1)
         extras["compact_256m_gelem_s"] = round(nk / (c_ms * 1e-3) / 1e9, 2)
         extras["compact_256m_alg_gbs"] = round(cbytes / (c_ms * 1e-3) / 1e9, 1)
+        # the order-free form: atomic space claims per wave (the pages') and per workgroup
+        for claim, code in ds._binding.CLAIM.items():
+            u_ms = timed(lambda: L.ds_compact_unordered(ds.DS_UINT32, keys.data_ptr(), kout.data_ptr(),
+                                                        cnt.data_ptr(), nk, 0, 1 << 31, code, sh), reps=10)
+            if int(cnt.item()) != kept:
+                raise SystemExit(f"ds_compact_unordered per {claim}: count {int(cnt.item())} != {kept}")
+            extras[f"compact_unordered_per_{claim}_256m_us"] = round(u_ms * 1e3, 1)
         del keys, kout
 
     cpu = None

@@ -128,6 +128,24 @@ int ds_scan(int dtype, int inclusive, int algo, const void* d_in, void* d_out, i
 int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected, int64_t n,
                int cmp, uint64_t operand_bits, hipStream_t stream);
 
+/* Granularity of the space claims of ds_compact_unordered. */
+typedef enum {
+    DS_CLAIM_PER_WAVE = 0,     /* one atomic add per 64-lane wave, as the pages' warp-aggregated atomic */
+    DS_CLAIM_PER_WORKGROUP = 1 /* the four waves' counts summed in LDS, one atomic add per workgroup */
+} ds_claim;
+
+/*
+ * Stream compaction that does not keep the input order: d_out[0 .. k) holds
+ * every kept element, in an unspecified order, and k goes to
+ * *d_num_selected. Each wave ranks its kept elements with a ballot and claims
+ * room for them with one atomic add on *d_num_selected ("Prefix sum and other
+ * parallel patterns", section "Stream compaction", warp-aggregated atomic).
+ * Arguments as compact_if, plus `claim` (ds_claim); d_out must not overlap
+ * d_in at all. *d_num_selected is the claim counter, cleared by the call.
+ */
+int ds_compact_unordered(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected, int64_t n,
+                         int cmp, uint64_t operand_bits, int claim, hipStream_t stream);
+
 /*
  * Copy of nbytes from d_in to d_out with the same launch shape, 16-byte
  * accesses and tile size as the 4-byte scan: the practical bandwidth ceiling

@@ -21,7 +21,7 @@ CMP = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
 ALGO = {"default": 0, "lookback": 1, "three_pass": 2}
 DS_OK = 0
 
-EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
+EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_compact_unordered", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
            "ds_tile_elems", "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace",
            "ds_version"]
 TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4}
@@ -41,6 +41,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ds_scan.restype = I
     L.compact_if.argtypes = [I, P, P, P, I64, I, ctypes.c_uint64, P]
     L.compact_if.restype = I
+    L.ds_compact_unordered.argtypes = [I, P, P, P, I64, I, ctypes.c_uint64, I, P]
+    L.ds_compact_unordered.restype = I
     L.ds_copy.argtypes = [P, P, I64, P]
     L.ds_copy.restype = I
     L.ds_tile_scan.argtypes = [I, I, P, P, P, I64, P]
@@ -176,6 +178,27 @@ def compact_if(x: torch.Tensor, cmp: str, operand, out: torch.Tensor | None = No
     with torch.cuda.device(x.device):
         _check(lib.compact_if(code, x.data_ptr(), out.data_ptr(), num_selected.data_ptr(), x.numel(), CMP[cmp],
                               operand_bits(x.dtype, operand), _stream_handle(x, stream)), "compact_if")
+    return out, num_selected
+
+
+CLAIM = {"wave": 0, "workgroup": 1}
+
+
+def compact_unordered(x: torch.Tensor, cmp: str, operand, out: torch.Tensor | None = None,
+                      num_selected: torch.Tensor | None = None, *, claim: str = "workgroup", stream=None):
+    """Compaction in no particular order (atomic space claims); returns (out, num_selected)."""
+    _check_tensor(x, "x")
+    code = dtype_code(x.dtype)
+    out = torch.empty_like(x) if out is None else out
+    num_selected = torch.empty(1, dtype=torch.int64, device=x.device) if num_selected is None else num_selected
+    _check_tensor(out, "out")
+    _check_tensor(num_selected, "num_selected")
+    if out.dtype != x.dtype or out.numel() < x.numel() or num_selected.dtype != torch.int64:
+        raise ValueError("out must match x and hold x.numel() elements; num_selected must be int64")
+    with torch.cuda.device(x.device):
+        _check(lib.ds_compact_unordered(code, x.data_ptr(), out.data_ptr(), num_selected.data_ptr(), x.numel(),
+                                        CMP[cmp], operand_bits(x.dtype, operand), CLAIM[claim],
+                                        _stream_handle(x, stream)), "ds_compact_unordered")
     return out, num_selected
 
 

@@ -197,6 +197,29 @@ int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
+int ds_compact_unordered(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected, int64_t n, int cmp,
+                         uint64_t operand_bits, int claim, hipStream_t stream)
+{
+    if (!valid_dtype(dtype)) return DS_ERR_UNSUPPORTED_DTYPE;
+    if (cmp < DS_LT || cmp > DS_NE) return DS_ERR_INVALID_VALUE;
+    if (claim != DS_CLAIM_PER_WAVE && claim != DS_CLAIM_PER_WORKGROUP) return DS_ERR_INVALID_VALUE;
+    if (!d_num_selected || n < 0) return DS_ERR_INVALID_VALUE;
+    if (((uintptr_t)d_num_selected) % 8) return DS_ERR_MISALIGNED;
+    if (n >= ((int64_t)1 << 32)) return DS_ERR_TOO_LARGE;
+    int st = check_io(dtype, d_in, d_out, n, false);  // out is written in any order: never in place
+    if (st != DS_OK) return st;
+    if (n == 0) {
+        static const int64_t zero = 0;
+        return hipMemcpyAsync(d_num_selected, &zero, sizeof(zero), hipMemcpyHostToDevice, stream) == hipSuccess
+                   ? DS_OK
+                   : DS_ERR_HIP;
+    }
+    return ds::launch_compact_unordered(kind_of(dtype), d_in, d_out, d_num_selected, n, cmp, operand_bits,
+                                        claim == DS_CLAIM_PER_WORKGROUP, stream) == hipSuccess
+               ? DS_OK
+               : DS_ERR_HIP;
+}
+
 int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream)
 {
     if (nbytes < 0 || (nbytes % 16)) return DS_ERR_INVALID_VALUE;

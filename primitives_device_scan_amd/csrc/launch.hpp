@@ -33,6 +33,9 @@ hipError_t launch_compact(ElemKind kind, const void* in, void* out, int64_t* num
                           int cmp, uint64_t operand_bits, const DevWs& ws, uint32_t spin_limit,
                           hipStream_t stream);
 
+hipError_t launch_compact_unordered(ElemKind kind, const void* in, void* out, int64_t* count, int64_t n, int cmp,
+                                    uint64_t operand_bits, bool per_workgroup, hipStream_t stream);
+
 hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t stream);
 
 // Exclusive scan of `count` tile totals in place (one workgroup, carried sum).

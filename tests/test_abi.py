@@ -93,6 +93,22 @@ def test_compact_validation(lib):
     assert lib.compact_if(0, None, B, C, 10, 0, 0, None) == 1
 
 
+def test_compact_unordered_validation(lib):
+    C = 0x7F0000200000
+    f = lib.ds_compact_unordered
+    assert f(9, A, B, C, 10, 0, 0, 0, None) == 2
+    assert f(0, A, B, C, 10, 6, 0, 0, None) == 1     # bad cmp
+    assert f(0, A, B, C, 10, 0, 0, 2, None) == 1     # bad claim
+    assert f(0, A, B, C, 10, 0, 0, -1, None) == 1
+    assert f(0, A, B, None, 10, 0, 0, 1, None) == 1
+    assert f(0, A, B, C, -3, 0, 0, 1, None) == 1
+    assert f(0, A, B, C + 4, 10, 0, 0, 1, None) == 4
+    assert f(0, A, B, C, 1 << 32, 0, 0, 1, None) == 7
+    assert f(0, A, A, C, 10, 0, 0, 1, None) == 3     # never in place: the order is not kept
+    assert f(0, A, A + 4, C, 10, 0, 0, 0, None) == 3
+    assert f(0, None, B, C, 10, 0, 0, 0, None) == 1
+
+
 def test_copy_validation(lib):
     assert lib.ds_copy(A, B, 17, None) == 1
     assert lib.ds_copy(A, B, -16, None) == 1
