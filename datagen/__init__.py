@@ -16,6 +16,15 @@ Workloads (n, dtype, values), one documented seed each:
   int32_100m    int32, n = 100,000,007,  uniform integers in [-1000,1000], seed 4
   fp32_100m     fp32,  n = 100,000,007,  standard normal (Box-Muller),     seed 4
   compact_256m  uint32, n = 268,435,456, uniform over [0, 2**32),          seed 5
+                (also the keys of the counting-sort pass)
+  moe_64k       int32 router choices: 65,536 tokens x top-8 of 256 experts,
+                Zipf(1) expert popularity, distinct experts per token,  seed 6
+
+Router choices (moe_topk_ids): expert e gets popularity weight
+1 / rank(e)^skew, rank a seeded permutation of the experts; each token draws
+top_k distinct experts with probability in proportion to those weights
+(Gumbel top-k: the k largest log-weight + Gumbel-noise scores), listed
+highest score first.
 """
 from __future__ import annotations
 
@@ -34,6 +43,12 @@ WORKLOADS = {
     "int32_100m": (100_000_007, "int32", 4),
     "fp32_100m": (100_000_007, "float32", 4),
     "compact_256m": (268_435_456, "uint32", 5),
+}
+
+# MoE routing workloads: name -> (num_tokens, top_k, num_experts, block, skew, seed)
+MOE_WORKLOADS = {
+    "moe_64k": (65_536, 8, 256, 64, 1.0, 6),
+    "moe_decode": (256, 8, 256, 64, 1.0, 7),
 }
 
 
@@ -133,6 +148,30 @@ def quarter_twos_f32(n: int) -> np.ndarray:
 def mod8_plus1(n: int, dtype=np.float32) -> np.ndarray:
     """x_i = (i % 8) + 1."""
     return ((np.arange(n, dtype=np.int64) % 8) + 1).astype(dtype)
+
+
+def moe_topk_ids(seed: int, num_tokens: int, top_k: int, num_experts: int, skew: float = 1.0) -> np.ndarray:
+    """int32 [num_tokens, top_k]: distinct experts per token, Zipf(skew) popularity."""
+    assert 1 <= top_k <= num_experts
+    rank = np.empty(num_experts, dtype=np.int64)
+    rank[np.argsort(splitmix64(seed, 0, num_experts), kind="stable")] = np.arange(num_experts)
+    logw = -skew * np.log((rank + 1).astype(np.float64))
+    out = np.empty((num_tokens, top_k), dtype=np.int32)
+    step = max(1, _CHUNK // num_experts)
+    for t0 in range(0, num_tokens, step):
+        c = min(step, num_tokens - t0)
+        u = ((splitmix64(seed + 1, t0 * num_experts, c * num_experts) >> np.uint64(11)).astype(np.float64) + 0.5) \
+            * 2.0 ** -53
+        score = logw[None, :] - np.log(-np.log(u.reshape(c, num_experts)))
+        top = np.argpartition(-score, top_k - 1, axis=1)[:, :top_k]
+        order = np.argsort(-np.take_along_axis(score, top, axis=1), axis=1, kind="stable")
+        out[t0:t0 + c] = np.take_along_axis(top, order, axis=1)
+    return out
+
+
+def moe_workload(name: str) -> np.ndarray:
+    t, k, e, _, skew, seed = MOE_WORKLOADS[name]
+    return moe_topk_ids(seed, t, k, e, skew)
 
 
 def workload(name: str, n: int | None = None) -> np.ndarray:

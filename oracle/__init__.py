@@ -1,4 +1,5 @@
-"""Sequential CPU oracle for device-wide prefix sums and stream compaction.
+"""Sequential CPU oracle for device-wide prefix sums, stream compaction, the
+counting-sort pass of a radix sort and MoE alignment.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product library. The arithmetic
@@ -50,6 +51,12 @@ class Oracle:
             f = getattr(L, "oracle_compact_" + name)
             f.argtypes = [_P, _P, _I64, ctypes.c_int, ct]
             f.restype = ctypes.c_int64
+        if hasattr(L, "oracle_radix_pass_u32"):
+            L.oracle_radix_pass_u32.argtypes = [_P, _P, _P, _P, _I64, ctypes.c_int, ctypes.c_int]
+            L.oracle_radix_pass_u32.restype = None
+        if hasattr(L, "oracle_moe_align"):
+            L.oracle_moe_align.argtypes = [_P, _I64, ctypes.c_int, ctypes.c_int, _P, _P, _P, _I64]
+            L.oracle_moe_align.restype = ctypes.c_int64
 
     def scan(self, x: np.ndarray, inclusive: bool):
         """Integer input: the scan in x's dtype (wrapping). fp32 input: (y, s_abs) in fp64."""
@@ -82,6 +89,35 @@ class Oracle:
         return out[:k]
 
 
+    def radix_pass(self, keys: np.ndarray, shift: int, bits: int, vals: np.ndarray | None = None):
+        """Keys (uint32) ordered stably by the digit (key >> shift) & (2^bits - 1); vals follow."""
+        keys = np.ascontiguousarray(keys, dtype=np.uint32)
+        ko = np.empty_like(keys)
+        vo = None
+        vp = None
+        if vals is not None:
+            vals = np.ascontiguousarray(vals, dtype=np.uint32)
+            assert vals.size == keys.size
+            vo = np.empty_like(vals)
+            vp = vals.ctypes.data
+        self.lib.oracle_radix_pass_u32(keys.ctypes.data, vp, ko.ctypes.data, None if vo is None else vo.ctypes.data,
+                                       keys.size, shift, bits)
+        return ko, vo
+
+    def moe_align(self, ids: np.ndarray, num_experts: int, block: int):
+        """(counts[E], offsets[E+1], sorted[offsets[E]]) for int32 expert ids."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32).ravel()
+        n = ids.size
+        counts = np.empty(num_experts, dtype=np.int32)
+        offsets = np.empty(num_experts + 1, dtype=np.int32)
+        cap = n + num_experts * (block - 1)
+        srt = np.empty(max(cap, 1), dtype=np.int32)
+        total = self.lib.oracle_moe_align(ids.ctypes.data, n, num_experts, block, counts.ctypes.data,
+                                          offsets.ctypes.data, srt.ctypes.data, cap)
+        assert total >= 0
+        return counts, offsets, srt[:total]
+
+
 _default: Oracle | None = None
 
 
@@ -98,3 +134,11 @@ def scan(x: np.ndarray, inclusive: bool):
 
 def compact(x: np.ndarray, op: str, operand) -> np.ndarray:
     return default().compact(x, op, operand)
+
+
+def radix_pass(keys: np.ndarray, shift: int, bits: int, vals: np.ndarray | None = None):
+    return default().radix_pass(keys, shift, bits, vals)
+
+
+def moe_align(ids: np.ndarray, num_experts: int, block: int):
+    return default().moe_align(ids, num_experts, block)

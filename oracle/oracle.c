@@ -24,8 +24,20 @@
  * returns how many it kept ("Prefix sum and other parallel patterns",
  * section "Stream compaction" and its first exercise).
  *
- * Every function accepts y == x (in place): each x_i is read before y_i is
- * written.
+ * A counting-sort pass (the step a radix sort repeats once per digit, which
+ * the pages name as a user of the exclusive scan: "Day 32", closing section,
+ * and "Prefix sum and other parallel patterns", opening paragraph) orders
+ * 32-bit keys stably by one digit: count each digit, take the exclusive scan
+ * of the counts as each digit's first output slot, then place the elements in
+ * input order.
+ *
+ * MoE alignment ("Prefix sum and other parallel patterns", section "In LLMs:
+ * MoE token dispatch" and exercise 2): the number of assignments per expert,
+ * each expert's start as the exclusive scan of those counts rounded up to a
+ * multiple of the block size, and the assignment indices grouped by expert.
+ *
+ * The scans accept y == x (in place): each x_i is read before y_i is
+ * written. The counting-sort and MoE functions need distinct buffers.
  */
 #include <stdint.h>
 
@@ -128,4 +140,66 @@ int64_t oracle_compact_u64(const uint64_t* x, uint64_t* out, int64_t n, int op, 
         if (ORACLE_KEEP(x[i], op, c))
             out[k++] = x[i];
     return k;
+}
+
+/*
+ * Stable counting-sort pass over the digit d(k) = (k >> shift) & (2^bits - 1),
+ * 1 <= bits <= 8, 0 <= shift <= 31: keys_out holds the keys ordered by digit,
+ * equal digits in input order; vals (may be NULL) follow their keys.
+ */
+void oracle_radix_pass_u32(const uint32_t* keys, const uint32_t* vals, uint32_t* keys_out, uint32_t* vals_out,
+                           int64_t n, int shift, int bits)
+{
+    int64_t count[256] = {0};
+    int64_t next[256];
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int64_t i = 0; i < n; ++i)
+        count[(keys[i] >> shift) & mask]++;
+    int64_t run = 0;
+    for (int d = 0; d < 256; ++d) {
+        next[d] = run;
+        run += count[d];
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t d = (keys[i] >> shift) & mask;
+        const int64_t p = next[d]++;
+        keys_out[p] = keys[i];
+        if (vals)
+            vals_out[p] = vals[i];
+    }
+}
+
+/*
+ * ids: n expert indices (token-major, top_k per token); an id outside
+ * [0, num_experts) belongs to no expert. counts[e] = assignments of expert e;
+ * offsets[0] = 0 and offsets[e+1] = offsets[e] + counts[e] rounded up to a
+ * multiple of block; sorted[offsets[e] ...] = the indices i with ids[i] == e
+ * in increasing order, and the rest of expert e's block-rounded segment is n
+ * (the padding mark). Writes sorted[0 .. offsets[E]) and returns offsets[E],
+ * or -1 if that exceeds capacity. num_experts <= 1024.
+ */
+int64_t oracle_moe_align(const int32_t* ids, int64_t n, int num_experts, int block, int32_t* counts,
+                         int32_t* offsets, int32_t* sorted, int64_t capacity)
+{
+    int64_t next[1024];
+    for (int e = 0; e < num_experts; ++e)
+        counts[e] = 0;
+    for (int64_t i = 0; i < n; ++i)
+        if (ids[i] >= 0 && ids[i] < num_experts)
+            counts[ids[i]]++;
+    int64_t run = 0;
+    for (int e = 0; e < num_experts; ++e) {
+        offsets[e] = (int32_t)run;
+        next[e] = run;
+        run += (counts[e] + block - 1) / block * block;
+    }
+    offsets[num_experts] = (int32_t)run;
+    if (run > capacity)
+        return -1;
+    for (int64_t p = 0; p < run; ++p)
+        sorted[p] = (int32_t)n;
+    for (int64_t i = 0; i < n; ++i)
+        if (ids[i] >= 0 && ids[i] < num_experts)
+            sorted[next[ids[i]]++] = (int32_t)i;
+    return run;
 }

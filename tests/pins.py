@@ -15,6 +15,13 @@ Pins, none of which re-types the oracle's own loop:
   * wraparound: closed form for constant 2^30 int32 input, brute force mod
     2^64 for raw 64-bit draws;
   * compaction: brute-force filtering, count = excl(flags)[n-1] + flags[n-1].
+  * counting-sort pass: hand-worked case (tests/golden/counting_sort_examples.txt),
+    numpy's stable argsort of the digits, brute-force output positions on
+    tiny inputs, and four 8-bit passes from the low digit up = np.sort;
+  * MoE alignment: hand-worked cases, np.bincount of the valid ids, the
+    offsets' defining properties (multiples of the block, the smallest that
+    hold each expert's count), np.nonzero per expert, the padding mark, and
+    block = 1 reducing to numpy's stable argsort of the ids.
 """
 from __future__ import annotations
 
@@ -209,5 +216,91 @@ def check_compact(orc):
     assert np.array_equal(k, x[flags.astype(bool)])
 
 
+def parse_counting_sort_examples(path=os.path.join(GOLDEN, "counting_sort_examples.txt")):
+    blocks, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("["):
+            cur = {"name": line.strip("[]")}
+            blocks.append(cur)
+            continue
+        key, _, val = line.partition(":")
+        cur[key.strip()] = [int(v, 0) for v in val.split()]
+    return blocks
+
+
+RADIX_DIGITS = [(0, 8), (8, 8), (24, 8), (28, 4), (31, 1), (5, 3), (0, 1)]
+
+
+def check_radix_pass(orc):
+    for ex in parse_counting_sort_examples():
+        if "keys" not in ex:
+            continue
+        keys = np.array(ex["keys"], dtype=np.uint32)
+        ko, vo = orc.radix_pass(keys, ex["shift"][0], ex["bits"][0], np.arange(keys.size, dtype=np.uint32))
+        assert ko.tolist() == ex["keys_out"] and vo.tolist() == ex["order"], (ex["name"], ko, vo)
+    for n in (0, 1, 2, 7, 100, 1000, 4097):
+        for gen in ("uniform", "few"):
+            keys = datagen.keys_u32(800 + n, n) if gen == "uniform" else \
+                (datagen.uniform_int(900 + n, n, 0, 3).astype(np.uint32) * np.uint32(0x01010101))
+            vals = datagen.keys_u32(850 + n, n)
+            for shift, bits in RADIX_DIGITS:
+                d = (keys >> np.uint32(shift)) & np.uint32((1 << bits) - 1)
+                perm = np.argsort(d, kind="stable")
+                ko, vo = orc.radix_pass(keys, shift, bits, vals)
+                assert np.array_equal(ko, keys[perm]) and np.array_equal(vo, vals[perm]), (n, gen, shift, bits)
+                ko2, none = orc.radix_pass(keys, shift, bits)
+                assert none is None and np.array_equal(ko2, ko)
+    # brute force: element i lands after every smaller digit and every earlier equal digit
+    for n in range(0, 41):
+        keys = datagen.uniform_int(950 + n, n, 0, 5).astype(np.uint32) << np.uint32(3)
+        ko, vo = orc.radix_pass(keys, 3, 2, np.arange(n, dtype=np.uint32))
+        d = [(int(k) >> 3) & 3 for k in keys]
+        for i in range(n):
+            pos = sum(1 for j in range(n) if d[j] < d[i]) + sum(1 for j in range(i) if d[j] == d[i])
+            assert ko[pos] == keys[i] and vo[pos] == i, (n, i)
+    # least significant digit first: four stable 8-bit passes sort the keys
+    keys = datagen.keys_u32(977, 5000)
+    keys[::7] = keys[3]  # repeated keys: stability decides the order of their values
+    k, v = keys, np.arange(keys.size, dtype=np.uint32)
+    for shift in (0, 8, 16, 24):
+        k, v = orc.radix_pass(k, shift, 8, v)
+    assert np.array_equal(k, np.sort(keys)) and np.array_equal(v, np.argsort(keys, kind="stable"))
+
+
+def check_moe_align(orc):
+    for ex in parse_counting_sort_examples():
+        if "ids" not in ex:
+            continue
+        c, o, srt = orc.moe_align(np.array(ex["ids"], dtype=np.int32), ex["experts"][0], ex["block"][0])
+        assert c.tolist() == ex["counts"] and o.tolist() == ex["offsets"] and srt.tolist() == ex["sorted"], ex["name"]
+    cases = [(1, 1, 1, 1), (3, 2, 4, 4), (100, 2, 8, 16), (1000, 8, 64, 64), (513, 4, 256, 64), (2000, 1, 5, 3),
+             (257, 8, 511, 32)]
+    for t, k, e, block in cases:
+        for drop in (False, True):
+            ids = datagen.moe_topk_ids(60 + t, t, k, e).ravel()
+            if drop:  # ids that name no expert
+                ids = ids.copy()
+                ids[::5] = -1
+                ids[1::7] = e
+                ids[2::11] = 1 << 30
+            n = ids.size
+            counts, offsets, srt = orc.moe_align(ids, e, block)
+            valid = (ids >= 0) & (ids < e)
+            assert np.array_equal(counts, np.bincount(ids[valid], minlength=e)), (t, k, e)
+            span = np.diff(offsets.astype(np.int64))
+            assert offsets[0] == 0 and np.all(span % block == 0)
+            assert np.all(span >= counts) and np.all(span < counts.astype(np.int64) + block)
+            assert srt.size == offsets[-1]
+            for x in range(e):
+                seg = srt[offsets[x]:offsets[x + 1]]
+                assert np.array_equal(seg[:counts[x]], np.nonzero(ids == x)[0]), (t, k, e, x)
+                assert np.all(seg[counts[x]:] == n)
+            if block == 1:
+                assert np.array_equal(srt, np.nonzero(valid)[0][np.argsort(ids[valid], kind="stable")])
+
+
 ALL = [check_worked_examples, check_brute_int, check_brute_fp32, check_closed_forms,
-       check_invariants, check_wraparound, check_compact]
+       check_invariants, check_wraparound, check_compact, check_radix_pass, check_moe_align]

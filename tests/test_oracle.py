@@ -68,6 +68,18 @@ MUTANTS = [
     ("signed compare done unsigned", "int64_t oracle_compact_i32(const int32_t* x, int32_t* out, int64_t n, int op, int32_t c)",
      "int64_t oracle_compact_i32(const int32_t* x0, int32_t* out, int64_t n, int op, int32_t c0)\n"
      "#define x ((const uint32_t*)x0)\n#define c ((uint32_t)c0)"),
+    ("counting sort ignores the shift", "const uint32_t mask = (1u << bits) - 1u;",
+     "const uint32_t mask = (1u << bits) - 1u;\n    shift = 0;"),
+    ("counting sort places equal digits last-first",
+     "    for (int64_t i = 0; i < n; ++i) {\n        const uint32_t d = (keys[i] >> shift) & mask;",
+     "    for (int64_t i = n - 1; i >= 0; --i) {\n        const uint32_t d = (keys[i] >> shift) & mask;"),
+    ("values stay where they were", "vals_out[p] = vals[i];", "vals_out[p] = vals[p];"),
+    ("digit mask one bit short", "const uint32_t mask = (1u << bits) - 1u;", "const uint32_t mask = (1u << (bits - 1)) - 1u;"),
+    ("MoE offsets not rounded to the block", "run += (counts[e] + block - 1) / block * block;", "run += counts[e];"),
+    ("MoE rounds a full block up once more", "run += (counts[e] + block - 1) / block * block;", "run += (counts[e] + block) / block * block;"),
+    ("MoE padding marked 0", "sorted[p] = (int32_t)n;", "sorted[p] = 0;"),
+    ("MoE expert 0 takes the invalid ids", "        if (ids[i] >= 0 && ids[i] < num_experts)\n            counts[ids[i]]++;",
+     "        counts[ids[i] >= 0 && ids[i] < num_experts ? ids[i] : 0]++;"),
 ]
 
 
