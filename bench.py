@@ -170,6 +170,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--compact", action="store_true", help="also time compact_if on 268,435,456 uint32 keys")
+    ap.add_argument("--sort", action="store_true",
+                    help="also time the counting-sort pass on 268,435,456 uint32 keys and MoE alignment")
     ap.add_argument("--profile-only", action="store_true",
                     help="inputs, one check, then --steps scans and --steps copies; no timing (for rocprofv3 runs)")
     ap.add_argument("--no-check", action="store_true", help="with --profile-only: skip the oracle check")
@@ -329,6 +331,33 @@ def main():
                 raise SystemExit(f"ds_compact_unordered per {claim}: count {int(cnt.item())} != {kept}")
             extras[f"compact_unordered_per_{claim}_256m_us"] = round(u_ms * 1e3, 1)
         del keys, kout
+
+    if args.sort:
+        # one stable 8-bit counting-sort pass (a radix sort's step) over the compaction keys
+        nk = datagen.WORKLOADS["compact_256m"][0]
+        keys = torch.from_numpy(datagen.workload("compact_256m").view(np.int32)).to(dev)
+        vals = torch.from_numpy(datagen.keys_u32(8, nk).view(np.int32)).to(dev)
+        kout, vout = torch.empty_like(keys), torch.empty_like(vals)
+        for shift in (0, 24):
+            r_ms = timed(lambda: L.ds_radix_pass(keys.data_ptr(), kout.data_ptr(), None, None, nk, shift, 8, sh),
+                         reps=10)
+            extras[f"radix_pass_256m_shift{shift}_us"] = round(r_ms * 1e3, 1)
+            extras[f"radix_pass_256m_shift{shift}_alg_gbs"] = round(12 * nk / (r_ms * 1e-3) / 1e9, 1)
+        rv_ms = timed(lambda: L.ds_radix_pass(keys.data_ptr(), kout.data_ptr(), vals.data_ptr(), vout.data_ptr(), nk,
+                                              0, 8, sh), reps=10)
+        extras["radix_pass_kv_256m_us"] = round(rv_ms * 1e3, 1)
+        extras["radix_pass_kv_256m_alg_gbs"] = round(20 * nk / (rv_ms * 1e-3) / 1e9, 1)
+        del keys, vals, kout, vout
+        for name, (t, k, e, block, _, _) in sorted(datagen.MOE_WORKLOADS.items()):
+            ids = torch.from_numpy(datagen.moe_workload(name)).to(dev)
+            na = ids.numel()
+            cap = na + e * (block - 1)
+            counts = torch.empty(e, dtype=torch.int32, device=dev)
+            offsets = torch.empty(e + 1, dtype=torch.int32, device=dev)
+            srt = torch.empty(cap, dtype=torch.int32, device=dev)
+            m_ms = timed(lambda: L.ds_moe_align(ids.data_ptr(), na, e, block, counts.data_ptr(), offsets.data_ptr(),
+                                                srt.data_ptr(), cap, sh), reps=20)
+            extras[f"moe_align_{name}_us"] = round(m_ms * 1e3, 1)
 
     cpu = None
     if not args.no_cpu:

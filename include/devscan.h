@@ -147,6 +147,41 @@ int ds_compact_unordered(int dtype, const void* d_in, void* d_out, int64_t* d_nu
                          int cmp, uint64_t operand_bits, int claim, hipStream_t stream);
 
 /*
+ * One stable counting-sort pass, the step a radix sort repeats once per digit
+ * ("Day 32 -- The CUDA scan algorithm", closing section; "Prefix sum and other
+ * parallel patterns", opening paragraph): d_keys_out holds the n uint32 keys
+ * ordered by the digit (key >> shift) & (2^bits - 1), keys with equal digits
+ * in input order. d_vals_in / d_vals_out (both NULL, or both n uint32
+ * values) carry a value with each key. Three launches: per-tile digit counts
+ * into a digit-major table, the device-wide exclusive scan of that table,
+ * then a stable scatter. Four-byte aligned device pointers; no buffer may
+ * overlap another (DS_ERR_OVERLAP). 1 <= bits <= 8, 0 <= shift,
+ * shift + bits <= 32 (else DS_ERR_INVALID_VALUE); n < 2^32 (else
+ * DS_ERR_TOO_LARGE). Scratch: 2^bits x (number of tiles) words, a tile being
+ * 4,096 to 16,384 keys; cached per (device, stream) like the scan workspace.
+ */
+int ds_radix_pass(const uint32_t* d_keys_in, uint32_t* d_keys_out, const uint32_t* d_vals_in,
+                  uint32_t* d_vals_out, int64_t n, int shift, int bits, hipStream_t stream);
+
+/*
+ * MoE token alignment ("Prefix sum and other parallel patterns", section "In
+ * LLMs: MoE token dispatch" and exercise 2). d_topk_ids: n int32 expert ids,
+ * token-major (n = tokens x top_k); an id outside [0, num_experts) is
+ * dropped. Writes d_counts[e] = assignments of expert e, d_offsets[0] = 0 and
+ * d_offsets[e + 1] = d_offsets[e] + d_counts[e] rounded up to a multiple of
+ * `block` (the grouped GEMM's tile), and d_sorted_ids[d_offsets[e] + j] = the
+ * index i (into d_topk_ids) of expert e's j-th assignment in input order, the
+ * rest of expert e's segment = n (the padding mark). Entries of d_sorted_ids
+ * from d_offsets[num_experts] on are not written. The same counting-sort
+ * pass as ds_radix_pass with the expert id as the digit, plus a one-workgroup
+ * launch for the rounded offsets. 1 <= num_experts <= 511, block >= 1,
+ * capacity >= n + num_experts * (block - 1) (else DS_ERR_INVALID_VALUE); that
+ * bound < 2^31 (else DS_ERR_TOO_LARGE). Buffers must not overlap.
+ */
+int ds_moe_align(const int32_t* d_topk_ids, int64_t n, int num_experts, int block, int32_t* d_counts,
+                 int32_t* d_offsets, int32_t* d_sorted_ids, int64_t capacity, hipStream_t stream);
+
+/*
  * Copy of nbytes from d_in to d_out with the same launch shape, 16-byte
  * accesses and tile size as the 4-byte scan: the practical bandwidth ceiling
  * the scan is measured against (the "copy, no scan" row of "Day 32 -- The
@@ -202,7 +237,9 @@ typedef enum {
     DS_TILE_OF_SCAN_INCLUSIVE = 1, /* scan_inclusive, ds_scan look-back inclusive */
     DS_TILE_OF_THREE_PASS = 2,     /* DS_ALGO_THREE_PASS */
     DS_TILE_OF_COMPACT = 3,        /* compact_if */
-    DS_TILE_OF_LDS_TILE_SCAN = 4   /* ds_tile_scan / ds_tile_pipeline (4-byte types only) */
+    DS_TILE_OF_LDS_TILE_SCAN = 4,  /* ds_tile_scan / ds_tile_pipeline (4-byte types only) */
+    DS_TILE_OF_COUNTING_SORT = 5   /* ds_radix_pass / ds_moe_align: keys per chunk; a workgroup
+                                      takes one to four chunks (4-byte types only) */
 } ds_tile_of;
 
 /*

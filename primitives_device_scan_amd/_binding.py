@@ -21,10 +21,12 @@ CMP = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
 ALGO = {"default": 0, "lookback": 1, "three_pass": 2}
 DS_OK = 0
 
-EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_compact_unordered", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
+EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_compact_unordered", "ds_radix_pass",
+           "ds_moe_align", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
            "ds_tile_elems", "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace",
            "ds_version"]
-TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4}
+TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4,
+           "counting_sort": 5}
 TILE_VARIANTS = {"tree": 0, "tree_pad1": 1, "tree_pad2": 2, "hillis_steele": 3}
 
 
@@ -43,6 +45,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.compact_if.restype = I
     L.ds_compact_unordered.argtypes = [I, P, P, P, I64, I, ctypes.c_uint64, I, P]
     L.ds_compact_unordered.restype = I
+    L.ds_radix_pass.argtypes = [P, P, P, P, I64, I, I, P]
+    L.ds_radix_pass.restype = I
+    L.ds_moe_align.argtypes = [P, I64, I, I, P, P, P, I64, P]
+    L.ds_moe_align.restype = I
     L.ds_copy.argtypes = [P, P, I64, P]
     L.ds_copy.restype = I
     L.ds_tile_scan.argtypes = [I, I, P, P, P, I64, P]
@@ -200,6 +206,48 @@ def compact_unordered(x: torch.Tensor, cmp: str, operand, out: torch.Tensor | No
                                         CMP[cmp], operand_bits(x.dtype, operand), CLAIM[claim],
                                         _stream_handle(x, stream)), "ds_compact_unordered")
     return out, num_selected
+
+
+def radix_pass(keys: torch.Tensor, shift: int, bits: int, vals: torch.Tensor | None = None,
+               keys_out: torch.Tensor | None = None, vals_out: torch.Tensor | None = None, *, stream=None):
+    """One stable counting-sort pass over the digit (key >> shift) & (2^bits - 1) of 32-bit keys
+    (int32 or uint32 storage, compared as unsigned); returns (keys_out, vals_out or None)."""
+    _check_tensor(keys, "keys")
+    if keys.element_size() != 4 or keys.is_floating_point():
+        raise TypeError("keys must be 32-bit integers")
+    keys_out = torch.empty_like(keys) if keys_out is None else keys_out
+    _check_tensor(keys_out, "keys_out")
+    if vals is not None:
+        _check_tensor(vals, "vals")
+        vals_out = torch.empty_like(vals) if vals_out is None else vals_out
+        _check_tensor(vals_out, "vals_out")
+        if vals.element_size() != 4 or vals.numel() != keys.numel() or vals_out.numel() < keys.numel():
+            raise ValueError("vals must hold one 32-bit value per key")
+    if keys_out.numel() < keys.numel():
+        raise ValueError("keys_out is too small")
+    with torch.cuda.device(keys.device):
+        _check(lib.ds_radix_pass(keys.data_ptr(), keys_out.data_ptr(), None if vals is None else vals.data_ptr(),
+                                 None if vals is None else vals_out.data_ptr(), keys.numel(), shift, bits,
+                                 _stream_handle(keys, stream)), "ds_radix_pass")
+    return keys_out, (vals_out if vals is not None else None)
+
+
+def moe_align(topk_ids: torch.Tensor, num_experts: int, block: int, *, stream=None):
+    """MoE alignment of int32 expert ids [tokens, top_k]: returns (counts[E], offsets[E+1],
+    sorted_ids[capacity]); the first offsets[E] entries of sorted_ids are written."""
+    _check_tensor(topk_ids, "topk_ids")
+    if topk_ids.dtype != torch.int32:
+        raise TypeError("topk_ids must be int32")
+    n = topk_ids.numel()
+    cap = max(1, n + num_experts * (block - 1))
+    dev = topk_ids.device
+    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.ds_moe_align(topk_ids.data_ptr(), n, num_experts, block, counts.data_ptr(), offsets.data_ptr(),
+                                sorted_ids.data_ptr(), cap, _stream_handle(topk_ids, stream)), "ds_moe_align")
+    return counts, offsets, sorted_ids
 
 
 def copy(src: torch.Tensor, dst: torch.Tensor, *, stream=None) -> torch.Tensor:

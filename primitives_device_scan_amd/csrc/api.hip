@@ -15,11 +15,14 @@ namespace {
 using ds::Ctrl;
 using ds::DevWs;
 
-// Workspace layout: [Ctrl][status: 16 B per tile][totals: 8 B per tile].
+// Workspace layout: [Ctrl][status: 16 B per tile][totals: 8 B per tile];
+// `aux` is a separate scratch buffer for the counting-sort tables.
 struct Workspace {
     char* base = nullptr;
     int64_t tile_cap = 0;
     uint64_t lookback_launches = 0;  // launches that stamped an epoch since the last clear
+    char* aux = nullptr;
+    size_t aux_cap = 0;
 };
 
 std::mutex g_mu;
@@ -80,6 +83,54 @@ int get_workspace(hipStream_t stream, int64_t tiles, Workspace** out)
     }
     *out = &w;
     return DS_OK;
+}
+
+// Scratch of at least `bytes` for (current device, stream); its contents are
+// undefined (every user writes what it reads).
+int get_aux(hipStream_t stream, size_t bytes, char** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.aux_cap < bytes) {
+        size_t cap = w.aux_cap * 2 > bytes ? w.aux_cap * 2 : bytes;
+        if (cap < ((size_t)1 << 20)) cap = (size_t)1 << 20;
+        if (w.aux) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return DS_ERR_HIP;
+            (void)hipFree(w.aux);
+            w.aux = nullptr;
+            w.aux_cap = 0;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, cap) != hipSuccess) {
+            (void)hipGetLastError();
+            return DS_ERR_OUT_OF_MEMORY;
+        }
+        w.aux = static_cast<char*>(p);
+        w.aux_cap = cap;
+    }
+    *out = w.aux;
+    return DS_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
+// The look-back workspace for an exclusive uint32 scan of `words` entries
+// (none when it fits one tile).
+int scan_workspace_u32(hipStream_t stream, int64_t words, DevWs* dws, Workspace** w)
+{
+    const int64_t te = ds::tile_elems(ds::kU32, false);
+    const int64_t tiles = (words + te - 1) / te;
+    *dws = DevWs{nullptr, nullptr, nullptr};
+    *w = nullptr;
+    if (tiles <= 1) return DS_OK;
+    const int st = get_workspace(stream, tiles, w);
+    if (st == DS_OK) *dws = view(**w);
+    return st;
 }
 
 bool valid_dtype(int dtype) { return dtype >= DS_INT32 && dtype <= DS_UINT64; }
@@ -309,12 +360,81 @@ const char* ds_status_string(int status)
     }
 }
 
+int ds_radix_pass(const uint32_t* d_keys_in, uint32_t* d_keys_out, const uint32_t* d_vals_in, uint32_t* d_vals_out,
+                  int64_t n, int shift, int bits, hipStream_t stream)
+{
+    if (n < 0 || bits < 1 || bits > 8 || shift < 0 || shift > 31 || shift + bits > 32) return DS_ERR_INVALID_VALUE;
+    if ((d_vals_in == nullptr) != (d_vals_out == nullptr)) return DS_ERR_INVALID_VALUE;
+    if (n == 0) return DS_OK;
+    if (n >= ((int64_t)1 << 32)) return DS_ERR_TOO_LARGE;
+    if (!d_keys_in || !d_keys_out) return DS_ERR_INVALID_VALUE;
+    const void* ptrs[4] = {d_keys_in, d_keys_out, d_vals_in, d_vals_out};
+    for (const void* p : ptrs)
+        if ((uintptr_t)p % 4) return DS_ERR_MISALIGNED;
+    const size_t bytes = (size_t)n * 4;
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (ptrs[i] && ptrs[j] && overlaps(ptrs[i], bytes, ptrs[j], bytes)) return DS_ERR_OVERLAP;
+    const int64_t tiles = n > 0 ? (n + ds::sort_tile_elems(n) - 1) / ds::sort_tile_elems(n) : 0;
+    const int64_t words = ((int64_t)1 << bits) * tiles;
+    std::lock_guard<std::mutex> lock(g_mu);
+    char* aux = nullptr;
+    int st = get_aux(stream, (size_t)words * 4, &aux);
+    if (st != DS_OK) return st;
+    DevWs dws;
+    Workspace* w = nullptr;
+    st = scan_workspace_u32(stream, words, &dws, &w);
+    if (st != DS_OK) return st;
+    const hipError_t e = ds::launch_radix_pass(d_keys_in, d_vals_in, d_keys_out, d_vals_out, n, shift, bits,
+                                               reinterpret_cast<uint32_t*>(aux), dws, g_spin_limit, stream);
+    if (w && e == hipSuccess) ++w->lookback_launches;
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+int ds_moe_align(const int32_t* d_topk_ids, int64_t n, int num_experts, int block, int32_t* d_counts,
+                 int32_t* d_offsets, int32_t* d_sorted_ids, int64_t capacity, hipStream_t stream)
+{
+    if (n < 0 || block < 1 || num_experts < 1 || num_experts > ds::sort_max_buckets()) return DS_ERR_INVALID_VALUE;
+    if (!d_counts || !d_offsets || !d_sorted_ids || (n > 0 && !d_topk_ids)) return DS_ERR_INVALID_VALUE;
+    const int64_t worst = n + (int64_t)num_experts * (block - 1);
+    if (worst >= ((int64_t)1 << 31)) return DS_ERR_TOO_LARGE;
+    if (capacity < worst) return DS_ERR_INVALID_VALUE;
+    const void* ptrs[4] = {d_topk_ids, d_counts, d_offsets, d_sorted_ids};
+    const size_t sizes[4] = {(size_t)n * 4, (size_t)num_experts * 4, (size_t)(num_experts + 1) * 4,
+                             (size_t)capacity * 4};
+    for (int i = 0; i < 4; ++i) {
+        if ((uintptr_t)ptrs[i] % 4) return DS_ERR_MISALIGNED;
+        for (int j = i + 1; j < 4; ++j)
+            if (ptrs[i] && ptrs[j] && overlaps(ptrs[i], sizes[i], ptrs[j], sizes[j])) return DS_ERR_OVERLAP;
+    }
+    const int64_t tiles = n > 0 ? (n + ds::sort_tile_elems(n) - 1) / ds::sort_tile_elems(n) : 0;
+    const int64_t words = (int64_t)num_experts * tiles;
+    std::lock_guard<std::mutex> lock(g_mu);
+    char* aux = nullptr;
+    int st = get_aux(stream, (size_t)(2 * words + num_experts) * 4, &aux);
+    if (st != DS_OK) return st;
+    DevWs dws;
+    Workspace* w = nullptr;
+    st = scan_workspace_u32(stream, words, &dws, &w);
+    if (st != DS_OK) return st;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(aux);
+    uint32_t* slots = hist + words;
+    const ds::MoeOut out{d_counts, d_offsets, reinterpret_cast<int32_t*>(slots + words), d_sorted_ids, block,
+                         capacity};
+    const hipError_t e = ds::launch_moe_align(d_topk_ids, n, num_experts, out, hist, slots, dws, g_spin_limit,
+                                              stream);
+    if (w && e == hipSuccess && n > 0) ++w->lookback_launches;
+    return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
 void ds_release_workspace(void)
 {
     std::lock_guard<std::mutex> lock(g_mu);
     if (!g_ws.empty()) (void)hipDeviceSynchronize();
-    for (auto& kv : g_ws)
+    for (auto& kv : g_ws) {
         if (kv.second.base) (void)hipFree(kv.second.base);
+        if (kv.second.aux) (void)hipFree(kv.second.aux);
+    }
     g_ws.clear();
 }
 
@@ -328,6 +448,7 @@ int64_t ds_tile_elems(int dtype, int entry)
     case DS_TILE_OF_THREE_PASS: return ds::three_pass_tile_elems(b);
     case DS_TILE_OF_COMPACT: return ds::compact_tile_elems(b);
     case DS_TILE_OF_LDS_TILE_SCAN: return b == 4 ? ds::lds_tile_elems() : -1;
+    case DS_TILE_OF_COUNTING_SORT: return b == 4 ? ds::sort_chunk_elems() : -1;
     default: return -1;
     }
 }

@@ -1,0 +1,390 @@
+// counting_sort.hip -- one stable counting-sort pass: the step a radix sort
+// repeats once per digit, and the "histogram, exclusive scan, scatter" of MoE
+// token dispatch. The pages name both as users of the exclusive scan ("Day 32
+// -- The CUDA scan algorithm", closing section: a radix sort runs one scan per
+// digit pass; "Prefix sum and other parallel patterns", section "In LLMs: MoE
+// token dispatch" and exercise 2).
+//
+// Three launches, reduce-then-scan style:
+//   1. digit_count_kernel: each tile (one to four chunks of 4,096 keys)
+//      counts its digits in LDS and writes count[d * tiles + tile] -- a
+//      digit-major table;
+//   2. the device-wide exclusive scan of that table (the look-back scan): the
+//      entry (d, tile) becomes the first output slot of tile's digit-d keys;
+//   3. digit_scatter_kernel: each tile ranks its keys in input order -- a
+//      wave matches equal digits with one ballot per digit bit and counts the
+//      matching lanes below each lane -- stages the chunk in LDS ordered by
+//      digit, and writes each digit's run to its slot, so equal digits keep
+//      their input order (the pass is stable).
+// Bucket B (one past the last real digit) collects elements that belong to
+// no bucket: the ragged end of the last chunk and, for MoE, ids outside
+// [0, experts). It takes part in the ranking but is never written.
+#include "device_scan.hpp"
+#include "launch.hpp"
+
+namespace ds {
+
+constexpr int kSortItems = 16;                        // keys per lane per chunk
+constexpr int kSortChunk = kThreads * kSortItems;     // 4,096 keys
+constexpr int kSortMaxChunks = 4;                     // chunks per tile, at most
+constexpr int kSortMaxBuckets = 512;                  // real buckets + the spare one
+
+struct RadixDigit {
+    uint32_t shift, mask, buckets;
+    __device__ __forceinline__ uint32_t operator()(uint32_t k) const { return (k >> shift) & mask; }
+};
+
+// Expert ids: an id outside [0, experts) (negative ones included, as unsigned)
+// goes to the spare bucket.
+struct ExpertDigit {
+    uint32_t buckets;
+    __device__ __forceinline__ uint32_t operator()(uint32_t k) const { return k < buckets ? k : buckets; }
+};
+
+__device__ __forceinline__ uint32_t lanes_below_mask(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Lanes whose bucket equals this lane's: one ballot per bit of the real
+// bucket indices (a lane differs from another where their bits' ballots
+// disagree), the spare bucket told apart by a ballot of its own. Every lane
+// of the wave takes part.
+template <int BITS>
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, uint32_t spare)
+{
+    const bool is_spare = d == spare;
+    const uint64_t spare_lanes = ballot(is_spare);
+    uint32_t lo = (uint32_t)spare_lanes, hi = (uint32_t)(spare_lanes >> 32);
+#pragma unroll
+    for (int b = 0; b < BITS; ++b) {
+        const int32_t mine = __builtin_amdgcn_sbfe((int32_t)d, b, 1);  // 0, or all ones where bit b is set
+        const uint64_t set = ballot(mine != 0);
+        lo |= (uint32_t)set ^ (uint32_t)mine;
+        hi |= (uint32_t)(set >> 32) ^ (uint32_t)mine;
+    }
+    const uint64_t same = ~(((uint64_t)hi << 32) | lo);
+    return is_spare ? spare_lanes : same;
+}
+
+template <typename DIG, bool VEC>
+__global__ __launch_bounds__(kThreads) void digit_count_kernel(const uint32_t* __restrict__ keys, int64_t n,
+                                                                 DIG dig, int tile_elems,
+                                                                 uint32_t* __restrict__ table, int64_t tiles)
+{
+    __shared__ uint32_t hist[kWaves][kSortMaxBuckets];
+    const uint32_t B = dig.buckets;
+    const int wave = (int)(threadIdx.x / kWave);
+    for (uint32_t i = threadIdx.x; i < kWaves * kSortMaxBuckets; i += kThreads) (&hist[0][0])[i] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * tile_elems;
+    if (VEC && base + tile_elems <= n) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(keys + base);
+#pragma unroll 4
+        for (int v = threadIdx.x; v < tile_elems / 4; v += kThreads) {
+            const u32x4 k = __builtin_nontemporal_load(p + v);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t d = dig(k[j]);
+                if (d < B) atomicAdd(&hist[wave][d], 1u);
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < tile_elems; i += kThreads) {
+            if (base + i >= n) break;
+            const uint32_t d = dig(keys[base + i]);
+            if (d < B) atomicAdd(&hist[wave][d], 1u);
+        }
+    }
+    __syncthreads();
+    for (uint32_t d = threadIdx.x; d < B; d += kThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c += hist[w][d];
+        table[(int64_t)d * tiles + blockIdx.x] = c;
+    }
+}
+
+// Exclusive scan over the workgroup of one value per thread (256 threads);
+// returns this thread's exclusive prefix and sets `total`.
+__device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t* s_wave, uint32_t& total)
+{
+    const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+    const uint32_t incl = wave_inclusive_scan(v);
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t t = s_wave[w];
+        if (w < wave) before += t;
+        all += t;
+    }
+    total = all;
+    return before + incl - v;
+}
+
+// Buckets d0 = 2t and d1 = 2t + 1 of thread t: the four waves' counts in
+// `cnt` become each wave's first staging position for the bucket; gdelta[d]
+// becomes (output slot of the chunk's first bucket-d key) - (its staging
+// position); gbase[d] moves past this chunk's bucket-d keys.
+__device__ __forceinline__ void chunk_bases(uint32_t (*cnt)[kSortMaxBuckets], uint32_t* gbase, uint32_t* gdelta,
+                                            uint32_t* s_wave, uint32_t* s_real, uint32_t B)
+{
+    const uint32_t d0 = 2 * threadIdx.x, d1 = d0 + 1;
+    uint32_t p0[kWaves], p1[kWaves], tot0 = 0, tot1 = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        p0[w] = tot0;
+        p1[w] = tot1;
+        if (d0 <= B) tot0 += cnt[w][d0];
+        if (d1 <= B) tot1 += cnt[w][d1];
+    }
+    uint32_t all;
+    const uint32_t start0 = block_exclusive_u32(tot0 + tot1, s_wave, all);
+    const uint32_t start1 = start0 + tot0;
+    if (d0 <= B) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) cnt[w][d0] = start0 + p0[w];
+        if (d0 < B) {
+            gdelta[d0] = gbase[d0] - start0;
+            gbase[d0] += tot0;
+        } else {
+            *s_real = start0;  // keys of real buckets come first in the staging order
+        }
+    }
+    if (d1 <= B) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) cnt[w][d1] = start1 + p1[w];
+        if (d1 < B) {
+            gdelta[d1] = gbase[d1] - start1;
+            gbase[d1] += tot1;
+        } else {
+            *s_real = start1;
+        }
+    }
+}
+
+// Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b mod 8).
+// Renumbering them so that each XCD takes a contiguous run of tiles puts the
+// two tiles that share a partly written cache line at each bucket's run
+// boundary on the same XCD, whose L2 then merges the two halves. Any order of
+// tiles is correct here: a tile's output slots come from the scanned table.
+__device__ __forceinline__ int64_t xcd_contiguous_tile()
+{
+    const uint32_t G = gridDim.x, b = blockIdx.x, x = b % 8u, q = G / 8u, r = G % 8u;
+    return (int64_t)(x * q + (x < r ? x : r) + b / 8u);
+}
+
+// VALS: 0 keys only; 1 values from vals_in follow the keys; 2 the value is the
+// element's index and only values are written (MoE: the assignment index).
+template <typename DIG, int VALS, int BITS>
+__global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out, int64_t n, DIG dig, int chunks,
+    const uint32_t* __restrict__ slots, const int32_t* __restrict__ slot_shift, int64_t tiles, int64_t out_cap)
+{
+    __shared__ uint32_t cnt[kWaves][kSortMaxBuckets];  // per wave: running count, then staging base
+    __shared__ uint32_t gbase[kSortMaxBuckets];        // next output slot of each bucket for this tile
+    __shared__ uint32_t gdelta[kSortMaxBuckets];       // output slot - staging position, this chunk
+    __shared__ uint32_t stage_k[kSortChunk];
+    __shared__ uint32_t stage_v[VALS ? kSortChunk : 1];
+    __shared__ uint32_t s_wave[kWaves];
+    __shared__ uint32_t s_real;
+    const uint32_t B = dig.buckets;  // real buckets; B itself is the spare one
+    const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+    const int64_t tile = xcd_contiguous_tile();
+    for (uint32_t d = threadIdx.x; d < B; d += kThreads)
+        gbase[d] = slots[(int64_t)d * tiles + tile] + (slot_shift ? (uint32_t)slot_shift[d] : 0u);
+
+    for (int c = 0; c < chunks; ++c) {
+        const int64_t chunk = (tile * chunks + c) * (int64_t)kSortChunk;
+        if (chunk >= n) break;  // uniform over the workgroup
+        for (uint32_t d = lane; d <= B; d += kWave) cnt[wave][d] = 0;
+        // This wave's 1,024 keys in input order: slot s of lane l is element s*64 + l.
+        const int64_t seg = chunk + (int64_t)wave * (kWave * kSortItems);
+        const bool whole = seg + kWave * kSortItems <= n;
+        uint32_t key[kSortItems], val[kSortItems], dr[kSortItems];
+        if (whole) {
+#pragma unroll
+            for (int s = 0; s < kSortItems; ++s) {
+                key[s] = keys[seg + s * kWave + lane];
+                if constexpr (VALS == 1) val[s] = vals_in[seg + s * kWave + lane];
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < kSortItems; ++s) {
+                const int64_t i = seg + s * kWave + lane;
+                key[s] = i < n ? keys[i] : 0u;
+                if constexpr (VALS == 1) val[s] = i < n ? vals_in[i] : 0u;
+            }
+        }
+        // Rank among this wave's keys of the same bucket, in input order.
+#pragma unroll
+        for (int s = 0; s < kSortItems; ++s) {
+            const int64_t i = seg + s * kWave + lane;
+            if constexpr (VALS == 2) val[s] = (uint32_t)i;
+            const uint32_t d = (whole || i < n) ? dig(key[s]) : B;
+            const uint64_t peers = match_digit<BITS>(d, B);
+            const uint32_t below = lanes_below_mask(peers);
+            const uint32_t run = cnt[wave][d];
+            if (below == 0) cnt[wave][d] = run + (uint32_t)__builtin_popcountll(peers);
+            dr[s] = (d << 16) | (run + below);
+        }
+        __syncthreads();
+        chunk_bases(cnt, gbase, gdelta, s_wave, &s_real, B);
+        __syncthreads();
+        // Stage the chunk ordered by bucket, equal buckets in input order.
+#pragma unroll
+        for (int s = 0; s < kSortItems; ++s) {
+            const uint32_t p = cnt[wave][dr[s] >> 16] + (dr[s] & 0xFFFFu);
+            if (p < (uint32_t)kSortChunk) {
+                stage_k[p] = key[s];
+                if constexpr (VALS != 0) stage_v[p] = val[s];
+            }
+        }
+        __syncthreads();
+        // Each bucket's run goes to its slots; the spare bucket's keys, staged
+        // last, are not written.
+        const uint32_t real = s_real;
+        for (uint32_t j = threadIdx.x; j < real; j += kThreads) {
+            const uint32_t k = stage_k[j];
+            const uint32_t d = dig(k);
+            const uint64_t pos = (uint64_t)(uint32_t)(gdelta[d] + j);
+            if (d < B && pos < (uint64_t)out_cap) {
+                if constexpr (VALS != 2) keys_out[pos] = k;
+                if constexpr (VALS != 0) vals_out[pos] = stage_v[j];
+            }
+        }
+    }
+}
+
+// One workgroup of 512 threads, thread e for expert e: counts from the
+// scanned table, offsets = exclusive scan of the counts rounded up to `block`,
+// the shift from the unpadded to the padded start, and the padding marks.
+constexpr int kMoeThreads = 512;
+
+__global__ __launch_bounds__(kMoeThreads) void moe_offsets_kernel(const uint32_t* __restrict__ hist,
+                                                                  const uint32_t* __restrict__ excl, int64_t tiles,
+                                                                  int experts, int block, int32_t n_mark,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ shift,
+                                                                  int32_t* __restrict__ sorted)
+{
+    __shared__ uint32_t s_wave[kMoeThreads / kWave];
+    const int e = (int)threadIdx.x, lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+    uint32_t c = 0, lo = 0;
+    if (e < experts && tiles > 0) {
+        lo = excl[(int64_t)e * tiles];
+        const uint32_t hi = e + 1 < experts ? excl[(int64_t)(e + 1) * tiles]
+                                            : excl[(int64_t)experts * tiles - 1] + hist[(int64_t)experts * tiles - 1];
+        c = hi - lo;
+    }
+    const uint32_t r = (c + (uint32_t)block - 1) / (uint32_t)block * (uint32_t)block;
+    const uint32_t incl = wave_inclusive_scan(r);
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kMoeThreads / kWave; ++w)
+        if (w < wave) before += s_wave[w];
+    const uint32_t off = before + incl - r;
+    if (e < experts) {
+        counts[e] = (int32_t)c;
+        offsets[e] = (int32_t)off;
+        shift[e] = (int32_t)(off - lo);
+        for (uint32_t j = c; j < r; ++j) sorted[off + j] = n_mark;
+    }
+    if (e == experts) offsets[e] = (int32_t)off;  // r = 0 here: the padded total
+}
+
+// Chunks per tile: four for large inputs (fewer table entries), fewer when
+// that would leave the GPU with under ~2,048 workgroups.
+static int chunks_for(int64_t n)
+{
+    const int64_t chunks = (n + kSortChunk - 1) / kSortChunk;
+    int c = (int)(chunks / 2048);
+    return c < 1 ? 1 : c > kSortMaxChunks ? kSortMaxChunks : c;
+}
+
+template <typename DIG, int VALS>
+static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out,
+                                      uint32_t* vals_out, int64_t n, DIG dig, uint32_t* hist, uint32_t* slots,
+                                      const int32_t* slot_shift, int64_t out_cap, const DevWs& ws,
+                                      uint32_t spin_limit, const MoeOut* moe, hipStream_t st)
+{
+    const int chunks = chunks_for(n);
+    const int tile_elems = chunks * kSortChunk;
+    const int64_t tiles = (n + tile_elems - 1) / tile_elems;
+    const dim3 grid((unsigned)tiles), block(kThreads);
+    if (aligned16(keys))
+        digit_count_kernel<DIG, true><<<grid, block, 0, st>>>(keys, n, dig, tile_elems, hist, tiles);
+    else
+        digit_count_kernel<DIG, false><<<grid, block, 0, st>>>(keys, n, dig, tile_elems, hist, tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_lookback_scan(kU32, false, hist, slots, (int64_t)dig.buckets * tiles, ws, spin_limit, st);
+    if (e != hipSuccess) return e;
+    if (moe) {
+        moe_offsets_kernel<<<dim3(1), dim3(kMoeThreads), 0, st>>>(hist, slots, tiles, (int)dig.buckets, moe->block,
+                                                                  (int32_t)n, moe->counts, moe->offsets,
+                                                                  moe->shift, moe->sorted);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int bits = dig.buckets > 1 ? 32 - __builtin_clz(dig.buckets - 1) : 0;
+#define DS_SCATTER(BITS)                                                                                      \
+    digit_scatter_kernel<DIG, VALS, BITS><<<grid, block, 0, st>>>(keys, vals_in, keys_out, vals_out, n, dig, chunks, \
+                                                                  slots, slot_shift, tiles, out_cap);         \
+    break
+    switch (bits) {
+    case 0: DS_SCATTER(0);
+    case 1: DS_SCATTER(1);
+    case 2: DS_SCATTER(2);
+    case 3: DS_SCATTER(3);
+    case 4: DS_SCATTER(4);
+    case 5: DS_SCATTER(5);
+    case 6: DS_SCATTER(6);
+    case 7: DS_SCATTER(7);
+    case 8: DS_SCATTER(8);
+    case 9: DS_SCATTER(9);
+    default: return hipErrorInvalidValue;
+    }
+#undef DS_SCATTER
+    return hipGetLastError();
+}
+
+int64_t sort_chunk_elems() { return kSortChunk; }
+int64_t sort_tile_elems(int64_t n) { return (int64_t)chunks_for(n) * kSortChunk; }
+int sort_max_buckets() { return kSortMaxBuckets - 1; }
+
+hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out, uint32_t* vals_out,
+                             int64_t n, int shift, int bits, uint32_t* table, const DevWs& ws, uint32_t spin_limit,
+                             hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    if (!table) return hipErrorInvalidValue;
+    const RadixDigit dig{(uint32_t)shift, (1u << bits) - 1u, 1u << bits};
+    if (vals_in)
+        return counting_sort_typed<RadixDigit, 1>(keys, vals_in, keys_out, vals_out, n, dig, table, table, nullptr,
+                                                  n, ws, spin_limit, nullptr, stream);
+    return counting_sort_typed<RadixDigit, 0>(keys, nullptr, keys_out, nullptr, n, dig, table, table, nullptr, n, ws,
+                                              spin_limit, nullptr, stream);
+}
+
+hipError_t launch_moe_align(const int32_t* ids, int64_t n, int experts, const MoeOut& out, uint32_t* hist,
+                            uint32_t* slots, const DevWs& ws, uint32_t spin_limit, hipStream_t stream)
+{
+    if (!hist || !slots || !out.shift) return hipErrorInvalidValue;
+    if (n == 0) {
+        moe_offsets_kernel<<<dim3(1), dim3(kMoeThreads), 0, stream>>>(hist, slots, 0, experts, out.block, 0,
+                                                                      out.counts, out.offsets, out.shift, out.sorted);
+        return hipGetLastError();
+    }
+    const ExpertDigit dig{(uint32_t)experts};
+    return counting_sort_typed<ExpertDigit, 2>((const uint32_t*)ids, nullptr, nullptr, (uint32_t*)out.sorted, n, dig,
+                                               hist, slots, out.shift, out.capacity, ws, spin_limit, &out, stream);
+}
+
+}  // namespace ds

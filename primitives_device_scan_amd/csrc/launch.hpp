@@ -1,5 +1,5 @@
-// launch.hpp -- host-side launchers of the scan kernels (kernels.hip), called
-// by the C ABI (api.cpp) after it has validated the arguments.
+// launch.hpp -- host-side launchers of the kernels in csrc/*.hip, called by
+// the C ABI (api.hip) after it has validated the arguments.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,6 +37,32 @@ hipError_t launch_compact_unordered(ElemKind kind, const void* in, void* out, in
                                     uint64_t operand_bits, bool per_workgroup, hipStream_t stream);
 
 hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t stream);
+
+// Counting-sort pass (radix sort step, MoE alignment): keys per chunk, keys
+// per workgroup tile for n keys (one to four chunks), and the most real
+// buckets a pass can have.
+int64_t sort_chunk_elems();
+int64_t sort_tile_elems(int64_t n);
+int sort_max_buckets();
+
+// table: (1 << bits) * tiles 32-bit words of scratch (the digit-major counts,
+// scanned in place); ws: look-back workspace for a scan of that many words.
+hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out, uint32_t* vals_out,
+                             int64_t n, int shift, int bits, uint32_t* table, const DevWs& ws, uint32_t spin_limit,
+                             hipStream_t stream);
+
+struct MoeOut {
+    int32_t* counts;    // [experts]
+    int32_t* offsets;   // [experts + 1]
+    int32_t* shift;     // [experts] scratch: padded start - unpadded start
+    int32_t* sorted;    // [capacity]
+    int block;
+    int64_t capacity;
+};
+
+// hist, slots: experts * tiles 32-bit words each of scratch.
+hipError_t launch_moe_align(const int32_t* ids, int64_t n, int experts, const MoeOut& out, uint32_t* hist,
+                            uint32_t* slots, const DevWs& ws, uint32_t spin_limit, hipStream_t stream);
 
 // Exclusive scan of `count` tile totals in place (one workgroup, carried sum).
 hipError_t launch_scan_totals(ElemKind kind, void* totals, int64_t count, hipStream_t stream);

@@ -109,6 +109,42 @@ def test_compact_unordered_validation(lib):
     assert f(0, None, B, C, 10, 0, 0, 0, None) == 1
 
 
+def test_radix_pass_validation(lib):
+    f = lib.ds_radix_pass
+    C, D = 0x7F0000200000, 0x7F0000300000
+    assert f(A, B, None, None, 10, 0, 0, None) == 1      # bits 0
+    assert f(A, B, None, None, 10, 0, 9, None) == 1      # bits 9
+    assert f(A, B, None, None, 10, -1, 8, None) == 1
+    assert f(A, B, None, None, 10, 32, 1, None) == 1
+    assert f(A, B, None, None, 10, 28, 8, None) == 1     # shift + bits > 32
+    assert f(A, B, C, None, 10, 0, 8, None) == 1         # values in without values out
+    assert f(A, B, None, None, -1, 0, 8, None) == 1
+    assert f(None, None, None, None, 0, 0, 8, None) == 0  # n == 0: nothing to do
+    assert f(A, B, None, None, 1 << 32, 0, 8, None) == 7
+    assert f(None, B, None, None, 10, 0, 8, None) == 1
+    assert f(A + 2, B, None, None, 10, 0, 8, None) == 4
+    assert f(A, B, C + 2, D, 10, 0, 8, None) == 4
+    assert f(A, A, None, None, 10, 0, 8, None) == 3      # never in place
+    assert f(A, A + 8, None, None, 10, 0, 8, None) == 3
+    assert f(A, B, C, B + 4, 10, 0, 8, None) == 3        # values out over keys out
+
+
+def test_moe_align_validation(lib):
+    f = lib.ds_moe_align
+    C, D, E = 0x7F0000200000, 0x7F0000300000, 0x7F0000400000
+    assert f(A, 100, 0, 64, B, C, D, 10000, None) == 1     # no experts
+    assert f(A, 100, 512, 64, B, C, D, 100000, None) == 1  # more experts than buckets
+    assert f(A, 100, 8, 0, B, C, D, 10000, None) == 1      # block 0
+    assert f(A, -1, 8, 64, B, C, D, 10000, None) == 1
+    assert f(A, 100, 8, 64, None, C, D, 10000, None) == 1
+    assert f(None, 100, 8, 64, B, C, D, 10000, None) == 1
+    assert f(A, 100, 8, 64, B, C, D, 100 + 8 * 63 - 1, None) == 1   # capacity below the worst case
+    assert f(A, 1 << 31, 8, 64, B, C, D, 1 << 32, None) == 7
+    assert f(A + 2, 100, 8, 64, B, C, D, 10000, None) == 4
+    assert f(A, 100, 8, 64, B, C, A + 200, 10000, None) == 3        # sorted ids over the input
+    assert f(A, 100, 8, 64, B, B + 16, D, 10000, None) == 3         # offsets over counts
+
+
 def test_copy_validation(lib):
     assert lib.ds_copy(A, B, 17, None) == 1
     assert lib.ds_copy(A, B, -16, None) == 1

@@ -1,0 +1,176 @@
+"""Parity of the counting-sort pass (ds_radix_pass) and MoE alignment
+(ds_moe_align), called through the C ABI, with the oracle: bit-exact keys,
+values, counts, offsets and grouped indices (the pass is stable, so the
+result is unique), and buffers past what the call defines left untouched."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import primitives_device_scan_amd as ds
+from gpu_util import assert_int_equal, cached_workload, from_dev, say, sentinel_fill, stream_handle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SORT_TILE = None
+
+
+def sort_tile():
+    global SORT_TILE
+    if SORT_TILE is None:
+        SORT_TILE = int(ds.lib.ds_tile_elems(1, ds._binding.TILE_OF["counting_sort"]))
+    return SORT_TILE
+
+
+def gpu_radix_pass(keys: np.ndarray, shift: int, bits: int, vals: np.ndarray | None = None):
+    n = keys.size
+    kin = to_dev(keys)
+    kout = torch.empty(max(n, 1) + 64, dtype=torch.int32, device="cuda")
+    sentinel_fill(kout)
+    vin = vout = None
+    if vals is not None:
+        vin = to_dev(vals)
+        vout = torch.empty(max(n, 1) + 64, dtype=torch.int32, device="cuda")
+        sentinel_fill(vout)
+    st = ds.lib.ds_radix_pass(kin.data_ptr(), kout.data_ptr(), None if vin is None else vin.data_ptr(),
+                              None if vout is None else vout.data_ptr(), n, shift, bits, stream_handle())
+    assert st == 0, ds.lib.ds_status_string(st)
+    torch.cuda.synchronize()
+    ko = from_dev(kout, np.uint32)
+    assert np.all(ko[n:] == 0xA5A5A5A5), "written past n"
+    vo = None
+    if vout is not None:
+        vo = from_dev(vout, np.uint32)
+        assert np.all(vo[n:] == 0xA5A5A5A5)
+        vo = vo[:n]
+    return ko[:n], vo
+
+
+def check_radix(keys, shift, bits, vals, what):
+    ko, vo = gpu_radix_pass(keys, shift, bits, vals)
+    wk, wv = oracle.radix_pass(keys, shift, bits, vals)
+    assert_int_equal(ko, wk, what + " keys")
+    if vals is not None:
+        assert_int_equal(vo, wv, what + " values")
+
+
+DIGITS = [(0, 8), (8, 8), (24, 8), (28, 4), (31, 1), (5, 3)]
+
+
+@pytest.mark.parametrize("shift,bits", DIGITS)
+def test_radix_pass_sizes(shift, bits):
+    T = sort_tile()
+    for n in (1, 7, 64, 4095, 4096, 4097, T - 1, T, T + 1, 3 * T + 5, 70 * T + 3):
+        keys = datagen.keys_u32(1000 + n, n)
+        vals = datagen.keys_u32(2000 + n, n)
+        check_radix(keys, shift, bits, vals, f"n={n} shift={shift} bits={bits}")
+        check_radix(keys, shift, bits, None, f"n={n} shift={shift} bits={bits} keys only")
+
+
+def test_radix_pass_skewed_digits():
+    T = sort_tile()
+    n = 5 * T + 77
+    few = (datagen.uniform_int(31, n, 0, 3).astype(np.uint32) * np.uint32(0x01010101))
+    same = np.full(n, 0xDEADBEEF, dtype=np.uint32)
+    one_hot = np.where(datagen.uniform_int(32, n, 0, 999) == 0, np.uint32(7), np.uint32(200))
+    for name, keys in (("four digits", few), ("all equal", same), ("one digit in 1000", one_hot)):
+        check_radix(keys, 0, 8, np.arange(n, dtype=np.uint32), name)
+
+
+@pytest.mark.parametrize("n", [20_000_003, 30_000_001])
+def test_radix_pass_two_and_three_chunk_tiles(n):
+    # workgroups take one to four 4,096-key chunks depending on n: these sizes take two and three
+    keys = datagen.keys_u32(n % 1000, n)
+    check_radix(keys, 8, 8, None, f"n={n}")
+
+
+def test_radix_pass_256m_keys():
+    keys = cached_workload("compact_256m")
+    say("radix pass: 268,435,456 uint32 keys, low 8-bit digit, with values")
+    vals = datagen.keys_u32(8, keys.size)
+    ko, vo = gpu_radix_pass(keys, 0, 8, vals)
+    wk, wv = oracle.radix_pass(keys, 0, 8, vals)
+    assert_int_equal(ko, wk, "256m keys")
+    assert_int_equal(vo, wv, "256m values")
+
+
+def test_four_passes_sort():
+    # least significant digit first: four stable 8-bit passes sort 32-bit keys
+    n = 1_000_003
+    keys = datagen.keys_u32(44, n)
+    keys[::5] = keys[1]
+    k, v = keys, np.arange(n, dtype=np.uint32)
+    for shift in (0, 8, 16, 24):
+        k, v = gpu_radix_pass(k, shift, 8, v)
+    assert_int_equal(k, np.sort(keys), "four passes: keys")
+    assert_int_equal(v, np.argsort(keys, kind="stable").astype(np.uint32), "four passes: values")
+
+
+def gpu_moe_align(ids: np.ndarray, experts: int, block: int):
+    ids = np.ascontiguousarray(ids, dtype=np.int32).ravel()
+    n = ids.size
+    cap = n + experts * (block - 1)
+    d_ids = to_dev(ids) if n else torch.zeros(1, dtype=torch.int32, device="cuda")
+    counts = torch.empty(experts, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(experts + 1, dtype=torch.int32, device="cuda")
+    srt = torch.empty(max(cap, 1), dtype=torch.int32, device="cuda")
+    for t in (counts, offsets, srt):
+        sentinel_fill(t)
+    st = ds.lib.ds_moe_align(d_ids.data_ptr(), n, experts, block, counts.data_ptr(), offsets.data_ptr(),
+                             srt.data_ptr(), max(cap, 1), stream_handle())
+    assert st == 0, ds.lib.ds_status_string(st)
+    torch.cuda.synchronize()
+    return counts.cpu().numpy(), offsets.cpu().numpy(), srt.cpu().numpy()
+
+
+def check_moe(ids, experts, block, what):
+    c, o, s = gpu_moe_align(ids, experts, block)
+    wc, wo, ws = oracle.moe_align(ids, experts, block)
+    assert_int_equal(c, wc, what + " counts")
+    assert_int_equal(o, wo, what + " offsets")
+    total = int(wo[-1])
+    assert_int_equal(s[:total], ws, what + " sorted ids")
+    assert np.all(s[total:].view(np.uint32) == 0xA5A5A5A5), what + ": written past offsets[E]"
+
+
+@pytest.mark.parametrize("name", sorted(datagen.MOE_WORKLOADS))
+def test_moe_workloads(name):
+    t, k, e, block, _, _ = datagen.MOE_WORKLOADS[name]
+    say("moe", name, t, "tokens x top", k, "of", e, "experts, block", block)
+    check_moe(datagen.moe_workload(name), e, block, name)
+
+
+@pytest.mark.parametrize("experts,top_k,block", [(1, 1, 1), (8, 2, 16), (64, 6, 64), (256, 8, 128), (511, 8, 32),
+                                                  (100, 3, 7)])
+def test_moe_shapes(experts, top_k, block):
+    T = sort_tile()
+    for tokens in (1, 5, 1000, T // top_k + 1, 3 * T // top_k + 11):
+        ids = datagen.moe_topk_ids(70 + tokens, tokens, top_k, experts)
+        check_moe(ids, experts, block, f"E={experts} k={top_k} block={block} tokens={tokens}")
+
+
+def test_moe_dropped_ids_and_empty():
+    ids = datagen.moe_topk_ids(5, 4099, 8, 64).ravel().copy()
+    ids[::5] = -1
+    ids[1::7] = 64
+    ids[2::11] = 1 << 30
+    check_moe(ids, 64, 16, "dropped ids")
+    check_moe(np.full(3000, -1, dtype=np.int32), 16, 8, "all dropped")
+    c, o, _ = gpu_moe_align(np.zeros(0, dtype=np.int32), 16, 8)
+    assert np.all(c == 0) and np.all(o == 0)
+
+
+def test_bindings():
+    x = torch.from_numpy(datagen.keys_u32(9, 100_000).view(np.int32)).cuda()
+    ko, vo = ds.radix_pass(x, 8, 8, vals=torch.arange(x.numel(), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    wk, wv = oracle.radix_pass(x.cpu().numpy().view(np.uint32), 8, 8, np.arange(x.numel(), dtype=np.uint32))
+    assert_int_equal(ko.cpu().numpy().view(np.uint32), wk, "binding keys")
+    assert_int_equal(vo.cpu().numpy().view(np.uint32), wv, "binding values")
+    ids = torch.from_numpy(datagen.moe_topk_ids(3, 500, 4, 32)).cuda()
+    c, o, s = ds.moe_align(ids, 32, 16)
+    torch.cuda.synchronize()
+    wc, wo, ws = oracle.moe_align(ids.cpu().numpy(), 32, 16)
+    assert np.array_equal(c.cpu().numpy(), wc) and np.array_equal(o.cpu().numpy(), wo)
+    assert np.array_equal(s.cpu().numpy()[:int(wo[-1])], ws)
