@@ -304,6 +304,22 @@ def main():
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in es]))
 
+    # Cold caches: a 1 GiB fill between launches evicts L2 and the memory-side
+    # cache; the timed value above is the back-to-back (warm) rate.
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    for name, fn in (("int32", scan_i), ("fp32", scan_f)):
+        cold = []
+        for r in range(10):
+            flush.fill_(r)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        extras[f"{name}_excl_cold_us_median"] = round(float(np.median(cold)) * 1e3, 2)
+    del flush
+
     cp_ms = timed(lambda: L.ds_copy(d_xi.data_ptr(), d_yi.data_ptr(), n * 4 // 16 * 16, sh))
     extras["copy_same_pattern_gbs"] = round(alg_bytes / (cp_ms * 1e-3) / 1e9, 1)
     extras["scan_over_copy"] = round(cp_ms / float(np.median(ms_i)), 4)

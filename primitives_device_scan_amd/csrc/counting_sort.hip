@@ -176,86 +176,171 @@ __device__ __forceinline__ int64_t xcd_contiguous_tile()
     return (int64_t)(x * q + (x < r ? x : r) + b / 8u);
 }
 
+// LDS of a workgroup that ranks and scatters 4,096-key chunks.
+template <int VALS>
+struct SortLds {
+    uint32_t cnt[kWaves][kSortMaxBuckets];  // per wave: running count, then staging base
+    uint32_t gbase[kSortMaxBuckets];        // next output slot of each bucket
+    uint32_t gdelta[kSortMaxBuckets];       // output slot - staging position, this chunk
+    uint32_t stage_k[kSortChunk];
+    uint32_t stage_v[VALS ? kSortChunk : 1];
+    uint32_t s_wave[kWaves];
+    uint32_t s_real;
+};
+
+// This wave's 1,024 keys of the chunk at `chunk`, in input order: slot s of
+// lane l is element s*64 + l of the wave's segment. All loads are issued
+// before any is used. Returns whether the whole segment lies below n.
+template <int VALS>
+__device__ __forceinline__ bool load_chunk(const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in,
+                                           int64_t n, int64_t chunk, uint32_t (&key)[kSortItems],
+                                           uint32_t (&val)[kSortItems])
+{
+    const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+    const int64_t seg = chunk + (int64_t)wave * (kWave * kSortItems);
+    const bool whole = seg + kWave * kSortItems <= n;
+    if (whole) {
+#pragma unroll
+        for (int s = 0; s < kSortItems; ++s) {
+            key[s] = keys[seg + s * kWave + lane];
+            if constexpr (VALS == 1) val[s] = vals_in[seg + s * kWave + lane];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < kSortItems; ++s) {
+            const int64_t i = seg + s * kWave + lane;
+            key[s] = i < n ? keys[i] : 0u;
+            if constexpr (VALS == 1) val[s] = i < n ? vals_in[i] : 0u;
+        }
+    }
+    return whole;
+}
+
 // VALS: 0 keys only; 1 values from vals_in follow the keys; 2 the value is the
 // element's index and only values are written (MoE: the assignment index).
+// One loaded chunk starting at `chunk` (< n): rank, stage, write; gbase must
+// hold each bucket's next output slot and is advanced past the chunk's keys.
+// Every thread of the workgroup calls it.
+template <typename DIG, int VALS, int BITS>
+__device__ __forceinline__ void rank_and_scatter(SortLds<VALS>& sh, const uint32_t (&key)[kSortItems],
+                                                 uint32_t (&val)[kSortItems], bool whole,
+                                                 uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
+                                                 int64_t n, DIG dig, int64_t chunk, int64_t out_cap)
+{
+    const uint32_t B = dig.buckets;  // real buckets; B itself is the spare one
+    const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+    const int64_t seg = chunk + (int64_t)wave * (kWave * kSortItems);
+    for (uint32_t d = lane; d <= B; d += kWave) sh.cnt[wave][d] = 0;
+    uint32_t dr[kSortItems];
+    // Rank among this wave's keys of the same bucket, in input order.
+#pragma unroll
+    for (int s = 0; s < kSortItems; ++s) {
+        const int64_t i = seg + s * kWave + lane;
+        if constexpr (VALS == 2) val[s] = (uint32_t)i;
+        const uint32_t d = (whole || i < n) ? dig(key[s]) : B;
+        const uint64_t peers = match_digit<BITS>(d, B);
+        const uint32_t below = lanes_below_mask(peers);
+        const uint32_t run = sh.cnt[wave][d];
+        if (below == 0) sh.cnt[wave][d] = run + (uint32_t)__builtin_popcountll(peers);
+        dr[s] = (d << 16) | (run + below);
+    }
+    __syncthreads();
+    chunk_bases(sh.cnt, sh.gbase, sh.gdelta, sh.s_wave, &sh.s_real, B);
+    __syncthreads();
+    // Stage the chunk ordered by bucket, equal buckets in input order.
+#pragma unroll
+    for (int s = 0; s < kSortItems; ++s) {
+        const uint32_t p = sh.cnt[wave][dr[s] >> 16] + (dr[s] & 0xFFFFu);
+        if (p < (uint32_t)kSortChunk) {
+            sh.stage_k[p] = key[s];
+            if constexpr (VALS != 0) sh.stage_v[p] = val[s];
+        }
+    }
+    __syncthreads();
+    // Each bucket's run goes to its slots; the spare bucket's keys, staged
+    // last, are not written.
+    const uint32_t real = sh.s_real;
+    for (uint32_t j = threadIdx.x; j < real; j += kThreads) {
+        const uint32_t k = sh.stage_k[j];
+        const uint32_t d = dig(k);
+        const uint64_t pos = (uint64_t)(uint32_t)(sh.gdelta[d] + j);
+        if (d < B && pos < (uint64_t)out_cap) {
+            if constexpr (VALS != 2) keys_out[pos] = k;
+            if constexpr (VALS != 0) vals_out[pos] = sh.stage_v[j];
+        }
+    }
+}
+
 template <typename DIG, int VALS, int BITS>
 __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, int64_t n, DIG dig, int chunks,
     const uint32_t* __restrict__ slots, const int32_t* __restrict__ slot_shift, int64_t tiles, int64_t out_cap)
 {
-    __shared__ uint32_t cnt[kWaves][kSortMaxBuckets];  // per wave: running count, then staging base
-    __shared__ uint32_t gbase[kSortMaxBuckets];        // next output slot of each bucket for this tile
-    __shared__ uint32_t gdelta[kSortMaxBuckets];       // output slot - staging position, this chunk
-    __shared__ uint32_t stage_k[kSortChunk];
-    __shared__ uint32_t stage_v[VALS ? kSortChunk : 1];
-    __shared__ uint32_t s_wave[kWaves];
-    __shared__ uint32_t s_real;
-    const uint32_t B = dig.buckets;  // real buckets; B itself is the spare one
-    const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+    __shared__ SortLds<VALS> sh;
     const int64_t tile = xcd_contiguous_tile();
-    for (uint32_t d = threadIdx.x; d < B; d += kThreads)
-        gbase[d] = slots[(int64_t)d * tiles + tile] + (slot_shift ? (uint32_t)slot_shift[d] : 0u);
-
+    for (uint32_t d = threadIdx.x; d < dig.buckets; d += kThreads)
+        sh.gbase[d] = slots[(int64_t)d * tiles + tile] + (slot_shift ? (uint32_t)slot_shift[d] : 0u);
     for (int c = 0; c < chunks; ++c) {
         const int64_t chunk = (tile * chunks + c) * (int64_t)kSortChunk;
         if (chunk >= n) break;  // uniform over the workgroup
-        for (uint32_t d = lane; d <= B; d += kWave) cnt[wave][d] = 0;
-        // This wave's 1,024 keys in input order: slot s of lane l is element s*64 + l.
-        const int64_t seg = chunk + (int64_t)wave * (kWave * kSortItems);
-        const bool whole = seg + kWave * kSortItems <= n;
-        uint32_t key[kSortItems], val[kSortItems], dr[kSortItems];
-        if (whole) {
+        uint32_t key[kSortItems], val[kSortItems];
+        const bool whole = load_chunk<VALS>(keys, vals_in, n, chunk, key, val);
+        rank_and_scatter<DIG, VALS, BITS>(sh, key, val, whole, keys_out, vals_out, n, dig, chunk, out_cap);
+    }
+}
+
+// MoE alignment of a few thousand ids in one workgroup and one launch: the
+// expert counts in LDS, the block-rounded offsets by a workgroup scan, the
+// padding marks, then the same chunk ranking and scatter as above, chunk
+// after chunk, from the offsets.
+constexpr int64_t kMoeOneLaunchMax = 2 * kSortChunk;
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void moe_align_one_launch_kernel(const uint32_t* __restrict__ ids, int64_t n,
+                                                                       ExpertDigit dig, int block,
+                                                                       int32_t* __restrict__ counts,
+                                                                       int32_t* __restrict__ offsets,
+                                                                       int32_t* __restrict__ sorted, int64_t cap)
+{
+    __shared__ SortLds<2> sh;
+    const uint32_t E = dig.buckets;
+    const int wave = (int)(threadIdx.x / kWave);
+    for (uint32_t i = threadIdx.x; i < kWaves * kSortMaxBuckets; i += kThreads) (&sh.cnt[0][0])[i] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+        const uint32_t d = dig(ids[i]);
+        if (d < E) atomicAdd(&sh.cnt[wave][d], 1u);
+    }
+    __syncthreads();
+    const uint32_t e0 = 2 * threadIdx.x, e1 = e0 + 1;
+    uint32_t c0 = 0, c1 = 0;
 #pragma unroll
-            for (int s = 0; s < kSortItems; ++s) {
-                key[s] = keys[seg + s * kWave + lane];
-                if constexpr (VALS == 1) val[s] = vals_in[seg + s * kWave + lane];
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < kSortItems; ++s) {
-                const int64_t i = seg + s * kWave + lane;
-                key[s] = i < n ? keys[i] : 0u;
-                if constexpr (VALS == 1) val[s] = i < n ? vals_in[i] : 0u;
-            }
-        }
-        // Rank among this wave's keys of the same bucket, in input order.
-#pragma unroll
-        for (int s = 0; s < kSortItems; ++s) {
-            const int64_t i = seg + s * kWave + lane;
-            if constexpr (VALS == 2) val[s] = (uint32_t)i;
-            const uint32_t d = (whole || i < n) ? dig(key[s]) : B;
-            const uint64_t peers = match_digit<BITS>(d, B);
-            const uint32_t below = lanes_below_mask(peers);
-            const uint32_t run = cnt[wave][d];
-            if (below == 0) cnt[wave][d] = run + (uint32_t)__builtin_popcountll(peers);
-            dr[s] = (d << 16) | (run + below);
-        }
-        __syncthreads();
-        chunk_bases(cnt, gbase, gdelta, s_wave, &s_real, B);
-        __syncthreads();
-        // Stage the chunk ordered by bucket, equal buckets in input order.
-#pragma unroll
-        for (int s = 0; s < kSortItems; ++s) {
-            const uint32_t p = cnt[wave][dr[s] >> 16] + (dr[s] & 0xFFFFu);
-            if (p < (uint32_t)kSortChunk) {
-                stage_k[p] = key[s];
-                if constexpr (VALS != 0) stage_v[p] = val[s];
-            }
-        }
-        __syncthreads();
-        // Each bucket's run goes to its slots; the spare bucket's keys, staged
-        // last, are not written.
-        const uint32_t real = s_real;
-        for (uint32_t j = threadIdx.x; j < real; j += kThreads) {
-            const uint32_t k = stage_k[j];
-            const uint32_t d = dig(k);
-            const uint64_t pos = (uint64_t)(uint32_t)(gdelta[d] + j);
-            if (d < B && pos < (uint64_t)out_cap) {
-                if constexpr (VALS != 2) keys_out[pos] = k;
-                if constexpr (VALS != 0) vals_out[pos] = stage_v[j];
-            }
-        }
+    for (int w = 0; w < kWaves; ++w) {
+        if (e0 < E) c0 += sh.cnt[w][e0];
+        if (e1 < E) c1 += sh.cnt[w][e1];
+    }
+    const uint32_t r0 = (c0 + block - 1) / block * block, r1 = (c1 + block - 1) / block * block;
+    uint32_t total;
+    const uint32_t off0 = block_exclusive_u32(r0 + r1, sh.s_wave, total), off1 = off0 + r0;
+    if (e0 < E) {
+        counts[e0] = (int32_t)c0;
+        offsets[e0] = (int32_t)off0;
+        sh.gbase[e0] = off0;
+        for (uint32_t j = c0; j < r0; ++j) sorted[off0 + j] = (int32_t)n;
+    }
+    if (e1 < E) {
+        counts[e1] = (int32_t)c1;
+        offsets[e1] = (int32_t)off1;
+        sh.gbase[e1] = off1;
+        for (uint32_t j = c1; j < r1; ++j) sorted[off1 + j] = (int32_t)n;
+    }
+    if (threadIdx.x == 0) offsets[E] = (int32_t)total;
+    __syncthreads();
+    for (int64_t chunk = 0; chunk < n; chunk += kSortChunk) {
+        uint32_t key[kSortItems], val[kSortItems];
+        const bool whole = load_chunk<0>(ids, nullptr, n, chunk, key, val);
+        rank_and_scatter<ExpertDigit, 2, BITS>(sh, key, val, whole, nullptr, (uint32_t*)sorted, n, dig, chunk, cap);
     }
 }
 
@@ -356,6 +441,7 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
 }
 
 int64_t sort_chunk_elems() { return kSortChunk; }
+int64_t moe_one_launch_max() { return kMoeOneLaunchMax; }
 int64_t sort_tile_elems(int64_t n) { return (int64_t)chunks_for(n) * kSortChunk; }
 int sort_max_buckets() { return kSortMaxBuckets - 1; }
 
@@ -377,12 +463,29 @@ hipError_t launch_moe_align(const int32_t* ids, int64_t n, int experts, const Mo
                             uint32_t* slots, const DevWs& ws, uint32_t spin_limit, hipStream_t stream)
 {
     if (!hist || !slots || !out.shift) return hipErrorInvalidValue;
-    if (n == 0) {
-        moe_offsets_kernel<<<dim3(1), dim3(kMoeThreads), 0, stream>>>(hist, slots, 0, experts, out.block, 0,
-                                                                      out.counts, out.offsets, out.shift, out.sorted);
+    const ExpertDigit dig{(uint32_t)experts};
+    if (n <= kMoeOneLaunchMax) {
+        const int bits = experts > 1 ? 32 - __builtin_clz((uint32_t)experts - 1) : 0;
+#define DS_MOE_ONE(BITS)                                                                                     \
+    moe_align_one_launch_kernel<BITS><<<dim3(1), dim3(kThreads), 0, stream>>>(                               \
+        (const uint32_t*)ids, n, dig, out.block, out.counts, out.offsets, out.sorted, out.capacity);       \
+    break
+        switch (bits) {
+        case 0: DS_MOE_ONE(0);
+        case 1: DS_MOE_ONE(1);
+        case 2: DS_MOE_ONE(2);
+        case 3: DS_MOE_ONE(3);
+        case 4: DS_MOE_ONE(4);
+        case 5: DS_MOE_ONE(5);
+        case 6: DS_MOE_ONE(6);
+        case 7: DS_MOE_ONE(7);
+        case 8: DS_MOE_ONE(8);
+        case 9: DS_MOE_ONE(9);
+        default: return hipErrorInvalidValue;
+        }
+#undef DS_MOE_ONE
         return hipGetLastError();
     }
-    const ExpertDigit dig{(uint32_t)experts};
     return counting_sort_typed<ExpertDigit, 2>((const uint32_t*)ids, nullptr, nullptr, (uint32_t*)out.sorted, n, dig,
                                                hist, slots, out.shift, out.capacity, ws, spin_limit, &out, stream);
 }

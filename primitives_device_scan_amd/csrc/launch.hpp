@@ -42,6 +42,7 @@ hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t st
 // per workgroup tile for n keys (one to four chunks), and the most real
 // buckets a pass can have.
 int64_t sort_chunk_elems();
+int64_t moe_one_launch_max();  // MoE inputs up to this many ids take one single-workgroup launch
 int64_t sort_tile_elems(int64_t n);
 int sort_max_buckets();
 

@@ -4,11 +4,12 @@
 // single-pass look-back.
 //
 // Tile layout (all kernels): a workgroup of 256 threads (4 waves of 64) owns
-// one tile of 16 KiB -- 4,096 four-byte or 2,048 eight-byte elements. Wave w
-// owns the w-th quarter of the tile; in it, lane l holds the 16-byte vectors
-// k*64 + l for k = 0..3. Every load and store instruction of a wave therefore
-// covers 1 KiB of contiguous memory, and the scan order inside the wave is
-// (vector k, lane, element in vector), which is the memory order.
+// one tile of VPT sixteen-byte vectors per thread (Shape<T, VPT>; each kernel
+// picks its VPT). Wave w owns the w-th quarter of the tile; in it, lane l
+// holds the 16-byte vectors k*64 + l for k = 0..VPT-1. Every load and store
+// instruction of a wave therefore covers 1 KiB of contiguous memory, and the
+// scan order inside the wave is (vector k, lane, element in vector), which is
+// the memory order.
 #pragma once
 
 #include <hip/hip_runtime.h>

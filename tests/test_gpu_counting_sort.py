@@ -150,6 +150,14 @@ def test_moe_shapes(experts, top_k, block):
         check_moe(ids, experts, block, f"E={experts} k={top_k} block={block} tokens={tokens}")
 
 
+@pytest.mark.parametrize("n", [4095, 4096, 4097, 8191, 8192, 8193, 12289])
+def test_moe_one_launch_boundary(n):
+    # up to 8,192 ids one single-workgroup launch aligns everything; above, the four-launch pipeline
+    ids = datagen.moe_topk_ids(n, n, 1, 100).ravel().copy()
+    ids[::13] = -3
+    check_moe(ids, 100, 16, f"n={n}")
+
+
 def test_moe_dropped_ids_and_empty():
     ids = datagen.moe_topk_ids(5, 4099, 8, 64).ravel().copy()
     ids[::5] = -1

@@ -93,6 +93,15 @@ def test_int32_100m_exclusive(algo):
     check_scan(x, False, gpu_scan(x, False, algo), f"int32_100m {algo}")
 
 
+@pytest.mark.parametrize("n", [1_048_576, 100_000_007])
+def test_int64_large(n):
+    # 64-bit values in [-2^40, 2^40]: two status words per tile carry the halves
+    x = datagen.uniform_i64(64, n, 40)
+    for inc in (False, True):
+        say(f"int64 n={n} inclusive={inc}")
+        assert_int_equal(gpu_scan(x, inc), oracle.scan(x, inc), f"int64 n={n} inc={inc}")
+
+
 def test_fp32_100m_exclusive():
     x = cached_workload("fp32_100m")
     for algo in ALGOS:
