@@ -216,6 +216,30 @@ __device__ __forceinline__ bool load_chunk(const uint32_t* __restrict__ keys, co
     return whole;
 }
 
+// Each key's rank among this wave's keys of the same bucket that come before
+// it, packed with its bucket as (bucket << 16) | rank; `cnt` (this wave's
+// per-bucket counts, zero on entry) ends as the wave's bucket counts. WHOLE:
+// every key of the wave's segment lies below n.
+template <typename DIG, int VALS, int BITS, bool WHOLE>
+__device__ __forceinline__ void rank_in_wave(uint32_t* cnt, const uint32_t (&key)[kSortItems],
+                                             uint32_t (&val)[kSortItems], uint32_t (&dr)[kSortItems], int64_t seg,
+                                             int64_t n, DIG dig)
+{
+    const uint32_t B = dig.buckets;
+    const int lane = lane_id();
+#pragma unroll
+    for (int s = 0; s < kSortItems; ++s) {
+        const int64_t i = seg + s * kWave + lane;
+        if constexpr (VALS == 2) val[s] = (uint32_t)i;
+        const uint32_t d = (WHOLE || i < n) ? dig(key[s]) : B;
+        const uint64_t peers = match_digit<BITS>(d, B);
+        const uint32_t below = lanes_below_mask(peers);
+        const uint32_t run = cnt[d];
+        if (below == 0) cnt[d] = run + (uint32_t)__builtin_popcountll(peers);
+        dr[s] = (d << 16) | (run + below);
+    }
+}
+
 // VALS: 0 keys only; 1 values from vals_in follow the keys; 2 the value is the
 // element's index and only values are written (MoE: the assignment index).
 // One loaded chunk starting at `chunk` (< n): rank, stage, write; gbase must
@@ -233,17 +257,10 @@ __device__ __forceinline__ void rank_and_scatter(SortLds<VALS>& sh, const uint32
     for (uint32_t d = lane; d <= B; d += kWave) sh.cnt[wave][d] = 0;
     uint32_t dr[kSortItems];
     // Rank among this wave's keys of the same bucket, in input order.
-#pragma unroll
-    for (int s = 0; s < kSortItems; ++s) {
-        const int64_t i = seg + s * kWave + lane;
-        if constexpr (VALS == 2) val[s] = (uint32_t)i;
-        const uint32_t d = (whole || i < n) ? dig(key[s]) : B;
-        const uint64_t peers = match_digit<BITS>(d, B);
-        const uint32_t below = lanes_below_mask(peers);
-        const uint32_t run = sh.cnt[wave][d];
-        if (below == 0) sh.cnt[wave][d] = run + (uint32_t)__builtin_popcountll(peers);
-        dr[s] = (d << 16) | (run + below);
-    }
+    if (whole)
+        rank_in_wave<DIG, VALS, BITS, true>(sh.cnt[wave], key, val, dr, seg, n, dig);
+    else
+        rank_in_wave<DIG, VALS, BITS, false>(sh.cnt[wave], key, val, dr, seg, n, dig);
     __syncthreads();
     chunk_bases(sh.cnt, sh.gbase, sh.gdelta, sh.s_wave, &sh.s_real, B);
     __syncthreads();
