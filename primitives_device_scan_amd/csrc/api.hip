@@ -411,7 +411,7 @@ int ds_moe_align(const int32_t* d_topk_ids, int64_t n, int num_experts, int bloc
     const int64_t words = (int64_t)num_experts * tiles;
     std::lock_guard<std::mutex> lock(g_mu);
     char* aux = nullptr;
-    int st = get_aux(stream, (size_t)(2 * words + num_experts) * 4, &aux);
+    int st = get_aux(stream, (size_t)(2 * words + 1) * 4, &aux);
     if (st != DS_OK) return st;
     DevWs dws;
     Workspace* w = nullptr;
@@ -419,8 +419,7 @@ int ds_moe_align(const int32_t* d_topk_ids, int64_t n, int num_experts, int bloc
     if (st != DS_OK) return st;
     uint32_t* hist = reinterpret_cast<uint32_t*>(aux);
     uint32_t* slots = hist + words;
-    const ds::MoeOut out{d_counts, d_offsets, reinterpret_cast<int32_t*>(slots + words), d_sorted_ids, block,
-                         capacity};
+    const ds::MoeOut out{d_counts, d_offsets, d_sorted_ids, block, capacity};
     const hipError_t e = ds::launch_moe_align(d_topk_ids, n, num_experts, out, hist, slots, dws, g_spin_limit,
                                               stream);
     if (w && e == hipSuccess && n > 0) ++w->lookback_launches;

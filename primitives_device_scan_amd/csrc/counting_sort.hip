@@ -16,6 +16,11 @@
 //      matching lanes below each lane -- stages the chunk in LDS ordered by
 //      digit, and writes each digit's run to its slot, so equal digits keep
 //      their input order (the pass is stable).
+// For MoE alignment every scatter workgroup also derives the experts' counts
+// and block-rounded offsets from the scanned table and shifts each expert's
+// slots to its padded start (workgroup 0 writes counts, offsets and padding
+// marks); up to kMoeOneLaunchMax ids, one workgroup does all of it in a
+// single launch (moe_align_one_launch_kernel).
 // Bucket B (one past the last real digit) collects elements that belong to
 // no bucket: the ragged end of the last chunk and, for MoE, ids outside
 // [0, experts). It takes part in the ranking but is never written.
@@ -288,16 +293,68 @@ __device__ __forceinline__ void rank_and_scatter(SortLds<VALS>& sh, const uint32
     }
 }
 
+// MoE outputs of the scatter: with hist set, every workgroup derives the
+// experts' block-rounded offsets from the scanned table and places its keys
+// at them; workgroup 0 also writes the counts, the offsets and the padding.
+struct MoeSlots {
+    const uint32_t* hist;  // the unscanned table (its last entry completes the total); null: a radix pass
+    int block;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted;
+};
+
+// gbase[e] for MoE: expert e's padded start plus the keys of e in earlier
+// tiles. Thread t takes experts 2t and 2t + 1.
+__device__ __forceinline__ void moe_bases(uint32_t* gbase, uint32_t* s_wave, const uint32_t* __restrict__ slots,
+                                          int64_t tiles, int64_t tile, uint32_t E, const MoeSlots& moe, int64_t n)
+{
+    const uint32_t e0 = 2 * threadIdx.x, e1 = e0 + 1;
+    const uint32_t last = slots[(int64_t)E * tiles - 1] + moe.hist[(int64_t)E * tiles - 1];
+    uint32_t lo0 = 0, lo1 = 0, c0 = 0, c1 = 0;
+    if (e0 < E) {
+        lo0 = slots[(int64_t)e0 * tiles];
+        c0 = (e0 + 1 < E ? slots[(int64_t)(e0 + 1) * tiles] : last) - lo0;
+    }
+    if (e1 < E) {
+        lo1 = slots[(int64_t)e1 * tiles];
+        c1 = (e1 + 1 < E ? slots[(int64_t)(e1 + 1) * tiles] : last) - lo1;
+    }
+    const uint32_t b = (uint32_t)moe.block;
+    const uint32_t r0 = (c0 + b - 1) / b * b, r1 = (c1 + b - 1) / b * b;
+    uint32_t total;
+    const uint32_t off0 = block_exclusive_u32(r0 + r1, s_wave, total), off1 = off0 + r0;
+    if (e0 < E) gbase[e0] = off0 + (slots[(int64_t)e0 * tiles + tile] - lo0);
+    if (e1 < E) gbase[e1] = off1 + (slots[(int64_t)e1 * tiles + tile] - lo1);
+    if (blockIdx.x == 0) {
+        if (e0 < E) {
+            moe.counts[e0] = (int32_t)c0;
+            moe.offsets[e0] = (int32_t)off0;
+            for (uint32_t j = c0; j < r0; ++j) moe.sorted[off0 + j] = (int32_t)n;
+        }
+        if (e1 < E) {
+            moe.counts[e1] = (int32_t)c1;
+            moe.offsets[e1] = (int32_t)off1;
+            for (uint32_t j = c1; j < r1; ++j) moe.sorted[off1 + j] = (int32_t)n;
+        }
+        if (threadIdx.x == 0) moe.offsets[E] = (int32_t)total;
+    }
+}
+
 template <typename DIG, int VALS, int BITS>
 __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, int64_t n, DIG dig, int chunks,
-    const uint32_t* __restrict__ slots, const int32_t* __restrict__ slot_shift, int64_t tiles, int64_t out_cap)
+    uint32_t* __restrict__ vals_out, int64_t n, DIG dig, int chunks, const uint32_t* __restrict__ slots,
+    MoeSlots moe, int64_t tiles, int64_t out_cap)
 {
     __shared__ SortLds<VALS> sh;
     const int64_t tile = xcd_contiguous_tile();
-    for (uint32_t d = threadIdx.x; d < dig.buckets; d += kThreads)
-        sh.gbase[d] = slots[(int64_t)d * tiles + tile] + (slot_shift ? (uint32_t)slot_shift[d] : 0u);
+    if (moe.hist) {
+        moe_bases(sh.gbase, sh.s_wave, slots, tiles, tile, dig.buckets, moe, n);
+    } else {
+        for (uint32_t d = threadIdx.x; d < dig.buckets; d += kThreads) sh.gbase[d] = slots[(int64_t)d * tiles + tile];
+    }
+    __syncthreads();
     for (int c = 0; c < chunks; ++c) {
         const int64_t chunk = (tile * chunks + c) * (int64_t)kSortChunk;
         if (chunk >= n) break;  // uniform over the workgroup
@@ -307,98 +364,98 @@ __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
     }
 }
 
-// MoE alignment of a few thousand ids in one workgroup and one launch: the
-// expert counts in LDS, the block-rounded offsets by a workgroup scan, the
-// padding marks, then the same chunk ranking and scatter as above, chunk
-// after chunk, from the offsets.
-constexpr int64_t kMoeOneLaunchMax = 2 * kSortChunk;
+// MoE alignment of up to kMoeOneLaunchMax ids in one launch of one
+// workgroup of 1,024 threads (16 waves). Wave w ranks the ids of its own
+// contiguous segment in input order (the same ballot match and per-wave LDS
+// counters as above), then thread e, for expert e, turns the 16 waves'
+// counts into the expert's count, its block-rounded offset (a workgroup
+// scan), the padding marks and each wave's first slot, and every lane writes
+// its ids' indices straight to their slots.
+constexpr int kMoeWaves = 16;
+constexpr int kMoeThreadsOne = kMoeWaves * kWave;
+constexpr int kMoeSlots = 8;  // ids per lane
+constexpr int64_t kMoeOneLaunchMax = (int64_t)kMoeThreadsOne * kMoeSlots;
 
 template <int BITS>
-__global__ __launch_bounds__(kThreads) void moe_align_one_launch_kernel(const uint32_t* __restrict__ ids, int64_t n,
-                                                                       ExpertDigit dig, int block,
-                                                                       int32_t* __restrict__ counts,
-                                                                       int32_t* __restrict__ offsets,
-                                                                       int32_t* __restrict__ sorted, int64_t cap)
+__global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(const uint32_t* __restrict__ ids,
+                                                                             int64_t n, ExpertDigit dig, int block,
+                                                                             int32_t* __restrict__ counts,
+                                                                             int32_t* __restrict__ offsets,
+                                                                             int32_t* __restrict__ sorted)
 {
-    __shared__ SortLds<2> sh;
+    __shared__ uint32_t cnt[kMoeWaves][kSortMaxBuckets];
+    __shared__ uint32_t s_count[kSortMaxBuckets], s_off[kSortMaxBuckets];
+    __shared__ uint32_t s_wave[kMoeWaves];
     const uint32_t E = dig.buckets;
-    const int wave = (int)(threadIdx.x / kWave);
-    for (uint32_t i = threadIdx.x; i < kWaves * kSortMaxBuckets; i += kThreads) (&sh.cnt[0][0])[i] = 0;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < n; i += kThreads) {
-        const uint32_t d = dig(ids[i]);
-        if (d < E) atomicAdd(&sh.cnt[wave][d], 1u);
-    }
-    __syncthreads();
-    const uint32_t e0 = 2 * threadIdx.x, e1 = e0 + 1;
-    uint32_t c0 = 0, c1 = 0;
+    const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+    for (uint32_t i = threadIdx.x; i < kMoeWaves * kSortMaxBuckets; i += kMoeThreadsOne) (&cnt[0][0])[i] = 0;
+    // Wave w's segment: seg_len ids from w * seg_len, seg_len a multiple of 64.
+    const int64_t seg_len = (n + kMoeThreadsOne - 1) / kMoeThreadsOne * kWave;
+    const int slots = (int)(seg_len / kWave);
+    const int64_t seg = (int64_t)wave * seg_len;
+    uint32_t key[kMoeSlots];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        if (e0 < E) c0 += sh.cnt[w][e0];
-        if (e1 < E) c1 += sh.cnt[w][e1];
+    for (int s = 0; s < kMoeSlots; ++s) {
+        const int64_t i = seg + s * kWave + lane;
+        key[s] = (s < slots && i < n) ? ids[i] : 0u;
     }
-    const uint32_t r0 = (c0 + block - 1) / block * block, r1 = (c1 + block - 1) / block * block;
-    uint32_t total;
-    const uint32_t off0 = block_exclusive_u32(r0 + r1, sh.s_wave, total), off1 = off0 + r0;
-    if (e0 < E) {
-        counts[e0] = (int32_t)c0;
-        offsets[e0] = (int32_t)off0;
-        sh.gbase[e0] = off0;
-        for (uint32_t j = c0; j < r0; ++j) sorted[off0 + j] = (int32_t)n;
-    }
-    if (e1 < E) {
-        counts[e1] = (int32_t)c1;
-        offsets[e1] = (int32_t)off1;
-        sh.gbase[e1] = off1;
-        for (uint32_t j = c1; j < r1; ++j) sorted[off1 + j] = (int32_t)n;
-    }
-    if (threadIdx.x == 0) offsets[E] = (int32_t)total;
     __syncthreads();
-    for (int64_t chunk = 0; chunk < n; chunk += kSortChunk) {
-        uint32_t key[kSortItems], val[kSortItems];
-        const bool whole = load_chunk<0>(ids, nullptr, n, chunk, key, val);
-        rank_and_scatter<ExpertDigit, 2, BITS>(sh, key, val, whole, nullptr, (uint32_t*)sorted, n, dig, chunk, cap);
+    uint32_t dr[kMoeSlots];
+#pragma unroll
+    for (int s = 0; s < kMoeSlots; ++s) {
+        if (s < slots) {  // uniform
+            const int64_t i = seg + s * kWave + lane;
+            const uint32_t d = i < n ? dig(key[s]) : E;
+            const uint64_t peers = match_digit<BITS>(d, E);
+            const uint32_t below = lanes_below_mask(peers);
+            const uint32_t run = cnt[wave][d];
+            if (below == 0) cnt[wave][d] = run + (uint32_t)__builtin_popcountll(peers);
+            dr[s] = (d << 16) | (run + below);
+        }
     }
-}
-
-// One workgroup of 512 threads, thread e for expert e: counts from the
-// scanned table, offsets = exclusive scan of the counts rounded up to `block`,
-// the shift from the unpadded to the padded start, and the padding marks.
-constexpr int kMoeThreads = 512;
-
-__global__ __launch_bounds__(kMoeThreads) void moe_offsets_kernel(const uint32_t* __restrict__ hist,
-                                                                  const uint32_t* __restrict__ excl, int64_t tiles,
-                                                                  int experts, int block, int32_t n_mark,
-                                                                  int32_t* __restrict__ counts,
-                                                                  int32_t* __restrict__ offsets,
-                                                                  int32_t* __restrict__ shift,
-                                                                  int32_t* __restrict__ sorted)
-{
-    __shared__ uint32_t s_wave[kMoeThreads / kWave];
-    const int e = (int)threadIdx.x, lane = lane_id(), wave = (int)(threadIdx.x / kWave);
-    uint32_t c = 0, lo = 0;
-    if (e < experts && tiles > 0) {
-        lo = excl[(int64_t)e * tiles];
-        const uint32_t hi = e + 1 < experts ? excl[(int64_t)(e + 1) * tiles]
-                                            : excl[(int64_t)experts * tiles - 1] + hist[(int64_t)experts * tiles - 1];
-        c = hi - lo;
+    __syncthreads();
+    // Thread e: expert e's count over the waves, its rounded offset, the
+    // waves' first slots, and the padding marks.
+    const uint32_t e = threadIdx.x;
+    uint32_t c = 0, pw[kMoeWaves];
+#pragma unroll
+    for (int w = 0; w < kMoeWaves; ++w) {
+        pw[w] = c;
+        if (e < E) c += cnt[w][e];
     }
-    const uint32_t r = (c + (uint32_t)block - 1) / (uint32_t)block * (uint32_t)block;
+    const uint32_t r = (c + block - 1) / block * block;
     const uint32_t incl = wave_inclusive_scan(r);
     if (lane == kWave - 1) s_wave[wave] = incl;
     __syncthreads();
     uint32_t before = 0;
 #pragma unroll
-    for (int w = 0; w < kMoeThreads / kWave; ++w)
+    for (int w = 0; w < kMoeWaves; ++w)
         if (w < wave) before += s_wave[w];
     const uint32_t off = before + incl - r;
-    if (e < experts) {
+    if (e < E) {
         counts[e] = (int32_t)c;
         offsets[e] = (int32_t)off;
-        shift[e] = (int32_t)(off - lo);
-        for (uint32_t j = c; j < r; ++j) sorted[off + j] = n_mark;
+#pragma unroll
+        for (int w = 0; w < kMoeWaves; ++w) cnt[w][e] = off + pw[w];
+        s_count[e] = c;
+        s_off[e] = off;
     }
-    if (e == experts) offsets[e] = (int32_t)off;  // r = 0 here: the padded total
+    if (e == E) offsets[E] = (int32_t)off;  // r = 0 here: the padded total
+    __syncthreads();
+    // Padding marks: wave w takes experts w, w + 16, ...; its lanes write the
+    // unused slots of the expert's rounded segment side by side.
+    for (uint32_t x = wave; x < E; x += kMoeWaves) {
+        const uint32_t cx = s_count[x], ox = s_off[x];
+        const uint32_t rx = (cx + block - 1) / block * block;
+        for (uint32_t j = cx + lane; j < rx; j += kWave) sorted[ox + j] = (int32_t)n;
+    }
+#pragma unroll
+    for (int s = 0; s < kMoeSlots; ++s) {
+        if (s < slots) {
+            const uint32_t d = dr[s] >> 16;
+            if (d < E) sorted[cnt[wave][d] + (dr[s] & 0xFFFFu)] = (int32_t)(seg + s * kWave + lane);
+        }
+    }
 }
 
 // Chunks per tile: four for large inputs (fewer table entries), fewer when
@@ -413,8 +470,8 @@ static int chunks_for(int64_t n)
 template <typename DIG, int VALS>
 static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out,
                                       uint32_t* vals_out, int64_t n, DIG dig, uint32_t* hist, uint32_t* slots,
-                                      const int32_t* slot_shift, int64_t out_cap, const DevWs& ws,
-                                      uint32_t spin_limit, const MoeOut* moe, hipStream_t st)
+                                      const MoeSlots& moe, int64_t out_cap, const DevWs& ws, uint32_t spin_limit,
+                                      hipStream_t st)
 {
     const int chunks = chunks_for(n);
     const int tile_elems = chunks * kSortChunk;
@@ -428,17 +485,10 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
     if (e != hipSuccess) return e;
     e = launch_lookback_scan(kU32, false, hist, slots, (int64_t)dig.buckets * tiles, ws, spin_limit, st);
     if (e != hipSuccess) return e;
-    if (moe) {
-        moe_offsets_kernel<<<dim3(1), dim3(kMoeThreads), 0, st>>>(hist, slots, tiles, (int)dig.buckets, moe->block,
-                                                                  (int32_t)n, moe->counts, moe->offsets,
-                                                                  moe->shift, moe->sorted);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     const int bits = dig.buckets > 1 ? 32 - __builtin_clz(dig.buckets - 1) : 0;
 #define DS_SCATTER(BITS)                                                                                      \
     digit_scatter_kernel<DIG, VALS, BITS><<<grid, block, 0, st>>>(keys, vals_in, keys_out, vals_out, n, dig, chunks, \
-                                                                  slots, slot_shift, tiles, out_cap);         \
+                                                                  slots, moe, tiles, out_cap);                \
     break
     switch (bits) {
     case 0: DS_SCATTER(0);
@@ -469,23 +519,24 @@ hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint
     if (n <= 0) return hipSuccess;
     if (!table) return hipErrorInvalidValue;
     const RadixDigit dig{(uint32_t)shift, (1u << bits) - 1u, 1u << bits};
+    const MoeSlots none{nullptr, 0, nullptr, nullptr, nullptr};
     if (vals_in)
-        return counting_sort_typed<RadixDigit, 1>(keys, vals_in, keys_out, vals_out, n, dig, table, table, nullptr,
-                                                  n, ws, spin_limit, nullptr, stream);
-    return counting_sort_typed<RadixDigit, 0>(keys, nullptr, keys_out, nullptr, n, dig, table, table, nullptr, n, ws,
-                                              spin_limit, nullptr, stream);
+        return counting_sort_typed<RadixDigit, 1>(keys, vals_in, keys_out, vals_out, n, dig, table, table, none, n, ws,
+                                                  spin_limit, stream);
+    return counting_sort_typed<RadixDigit, 0>(keys, nullptr, keys_out, nullptr, n, dig, table, table, none, n, ws,
+                                              spin_limit, stream);
 }
 
 hipError_t launch_moe_align(const int32_t* ids, int64_t n, int experts, const MoeOut& out, uint32_t* hist,
                             uint32_t* slots, const DevWs& ws, uint32_t spin_limit, hipStream_t stream)
 {
-    if (!hist || !slots || !out.shift) return hipErrorInvalidValue;
+    if (!hist || !slots) return hipErrorInvalidValue;
     const ExpertDigit dig{(uint32_t)experts};
     if (n <= kMoeOneLaunchMax) {
         const int bits = experts > 1 ? 32 - __builtin_clz((uint32_t)experts - 1) : 0;
 #define DS_MOE_ONE(BITS)                                                                                     \
-    moe_align_one_launch_kernel<BITS><<<dim3(1), dim3(kThreads), 0, stream>>>(                               \
-        (const uint32_t*)ids, n, dig, out.block, out.counts, out.offsets, out.sorted, out.capacity);       \
+    moe_align_one_launch_kernel<BITS><<<dim3(1), dim3(kMoeThreadsOne), 0, stream>>>(                        \
+        (const uint32_t*)ids, n, dig, out.block, out.counts, out.offsets, out.sorted);                     \
     break
         switch (bits) {
         case 0: DS_MOE_ONE(0);
@@ -503,8 +554,9 @@ hipError_t launch_moe_align(const int32_t* ids, int64_t n, int experts, const Mo
 #undef DS_MOE_ONE
         return hipGetLastError();
     }
+    const MoeSlots moe{hist, out.block, out.counts, out.offsets, out.sorted};
     return counting_sort_typed<ExpertDigit, 2>((const uint32_t*)ids, nullptr, nullptr, (uint32_t*)out.sorted, n, dig,
-                                               hist, slots, out.shift, out.capacity, ws, spin_limit, &out, stream);
+                                               hist, slots, moe, out.capacity, ws, spin_limit, stream);
 }
 
 }  // namespace ds

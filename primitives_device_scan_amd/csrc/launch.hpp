@@ -55,7 +55,6 @@ hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint
 struct MoeOut {
     int32_t* counts;    // [experts]
     int32_t* offsets;   // [experts + 1]
-    int32_t* shift;     // [experts] scratch: padded start - unpadded start
     int32_t* sorted;    // [capacity]
     int block;
     int64_t capacity;

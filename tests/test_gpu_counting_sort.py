@@ -169,6 +169,27 @@ def test_moe_dropped_ids_and_empty():
     assert np.all(c == 0) and np.all(o == 0)
 
 
+def test_radix_pass_two_streams():
+    # each (device, stream) has its own table and look-back workspace: two passes in flight at once
+    T = sort_tile()
+    n = 300 * T + 11
+    ka, kb = datagen.keys_u32(71, n), datagen.keys_u32(72, n)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for keys, st in ((ka, s1), (kb, s2)):
+        kin = to_dev(keys)
+        kout = torch.empty_like(kin)
+        outs.append((keys, kin, kout, st))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for keys, kin, kout, st in outs:
+            assert ds.lib.ds_radix_pass(kin.data_ptr(), kout.data_ptr(), None, None, n, 16, 8, st.cuda_stream) == 0
+    torch.cuda.synchronize()
+    for keys, kin, kout, st in outs:
+        wk, _ = oracle.radix_pass(keys, 16, 8)
+        assert_int_equal(from_dev(kout, np.uint32), wk, "two streams")
+
+
 def test_bindings():
     x = torch.from_numpy(datagen.keys_u32(9, 100_000).view(np.int32)).cuda()
     ko, vo = ds.radix_pass(x, 8, 8, vals=torch.arange(x.numel(), dtype=torch.int32, device="cuda"))
