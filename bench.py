@@ -413,7 +413,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "exclusive scan, int32 then fp32, n=100,000,007 each (int uniform [-1000,1000], "
                                "fp32 standard normal, seed 4)", "n": n, "algo": "single-pass decoupled look-back",
-                   "tile_elems": 16384, "workgroup": 256},
+                   "tile_elems": {"int32": int(L.ds_tile_elems(ds.DS_INT32, 0)),
+                                  "fp32": int(L.ds_tile_elems(ds.DS_FP32, 0))},
+                   "workgroup": 256},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": "lookback_scan_kernel",
