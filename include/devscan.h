@@ -1,13 +1,15 @@
 /*
- * devscan.h -- device-wide prefix sums (scans) and stream compaction for AMD
- * Instinct MI355X (gfx950), as a plain C ABI.
+ * devscan.h -- device-wide prefix sums (scans), stream compaction and two
+ * users of the scan built on one counting-sort pass (a radix-sort pass, MoE
+ * token alignment) for AMD Instinct MI355X (gfx950), as a plain C ABI.
  *
  * Every entry point takes device pointers and an element count, enqueues its
  * work on `stream` and returns without waiting for it. The caller owns every
  * pointer it passes and keeps the memory alive until the stream work is done.
  * The library owns only a small workspace per (device, stream): per-tile
- * status words, a launch epoch and, for the three-pass form, the tile
- * totals. It grows on demand and is freed by ds_release_workspace().
+ * status words, a launch epoch, for the three-pass form the tile totals, and
+ * for the counting-sort pass its digit-by-tile table. It grows on demand and
+ * is freed by ds_release_workspace().
  *
  * Errors. Argument errors are found on the host before any HIP call and
  * returned at once (DS_ERR_*); launch failures return DS_ERR_HIP. A fault
