@@ -12,8 +12,13 @@ seeded (datagen). Prints one JSON line:
              algorithmic bytes 2 * n * 4 per launch / mean launch time from
              HIP events on the launch stream
   cpu_baseline  the sequential CPU oracle on the host, same inputs
+  extras     the same-pattern copy, the three-pass scan, cold-cache scans,
+             and (unless --no-compact / --no-sort) compaction of 268,435,456
+             uint32 keys (ordered and both unordered forms), one 8-bit
+             counting-sort pass over those keys (with and without values) and
+             MoE alignment of two router workloads
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--compact]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-compact] [--no-sort]
 """
 from __future__ import annotations
 
@@ -169,9 +174,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--compact", action="store_true", help="also time compact_if on 268,435,456 uint32 keys")
-    ap.add_argument("--sort", action="store_true",
-                    help="also time the counting-sort pass on 268,435,456 uint32 keys and MoE alignment")
+    ap.add_argument("--compact", action="store_true", help=argparse.SUPPRESS)  # on by default
+    ap.add_argument("--sort", action="store_true", help=argparse.SUPPRESS)     # on by default
+    ap.add_argument("--no-compact", action="store_true",
+                    help="skip timing compact_if / ds_compact_unordered on 268,435,456 uint32 keys")
+    ap.add_argument("--no-sort", action="store_true",
+                    help="skip timing the counting-sort pass on 268,435,456 uint32 keys and MoE alignment")
     ap.add_argument("--profile-only", action="store_true",
                     help="inputs, one check, then --steps scans and --steps copies; no timing (for rocprofv3 runs)")
     ap.add_argument("--no-check", action="store_true", help="with --profile-only: skip the oracle check")
@@ -327,7 +335,7 @@ def main():
     extras["three_pass_int32_gelem_s"] = round(n / (tp_ms * 1e-3) / 1e9, 2)
     extras["three_pass_int32_alg_gbs"] = round(alg_bytes / (tp_ms * 1e-3) / 1e9, 1)
 
-    if args.compact:
+    if not args.no_compact:
         nk = datagen.WORKLOADS["compact_256m"][0]
         keys = torch.from_numpy(datagen.workload("compact_256m").view(np.int32)).to(dev)
         kout = torch.empty_like(keys)
@@ -348,7 +356,7 @@ def main():
             extras[f"compact_unordered_per_{claim}_256m_us"] = round(u_ms * 1e3, 1)
         del keys, kout
 
-    if args.sort:
+    if not args.no_sort:
         # one stable 8-bit counting-sort pass (a radix sort's step) over the compaction keys
         nk = datagen.WORKLOADS["compact_256m"][0]
         keys = torch.from_numpy(datagen.workload("compact_256m").view(np.int32)).to(dev)
