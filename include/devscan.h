@@ -156,8 +156,9 @@ int ds_compact_unordered(int dtype, const void* d_in, void* d_out, int64_t* d_nu
  * in input order. d_vals_in / d_vals_out (both NULL, or both n uint32
  * values) carry a value with each key. Three launches: per-tile digit counts
  * into a digit-major table, the device-wide exclusive scan of that table,
- * then a stable scatter. Four-byte aligned device pointers; no buffer may
- * overlap another (DS_ERR_OVERLAP). 1 <= bits <= 8, 0 <= shift,
+ * then a stable scatter. Four-byte aligned device pointers; an output may
+ * not overlap any other buffer (DS_ERR_OVERLAP), the two inputs may share
+ * memory. 1 <= bits <= 8, 0 <= shift,
  * shift + bits <= 32 (else DS_ERR_INVALID_VALUE); n < 2^32 (else
  * DS_ERR_TOO_LARGE). Scratch: 2^bits x (number of tiles) words, a tile being
  * 4,096 to 16,384 keys; cached per (device, stream) like the scan workspace.
