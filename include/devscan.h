@@ -161,7 +161,7 @@ int ds_compact_unordered(int dtype, const void* d_in, void* d_out, int64_t* d_nu
  * memory. 1 <= bits <= 8, 0 <= shift,
  * shift + bits <= 32 (else DS_ERR_INVALID_VALUE); n < 2^32 (else
  * DS_ERR_TOO_LARGE). Scratch: 2^bits x (number of tiles) words, a tile being
- * 4,096 to 16,384 keys; cached per (device, stream) like the scan workspace.
+ * 8,192 or 16,384 keys; cached per (device, stream) like the scan workspace.
  */
 int ds_radix_pass(const uint32_t* d_keys_in, uint32_t* d_keys_out, const uint32_t* d_vals_in,
                   uint32_t* d_vals_out, int64_t n, int shift, int bits, hipStream_t stream);
@@ -241,8 +241,9 @@ typedef enum {
     DS_TILE_OF_THREE_PASS = 2,     /* DS_ALGO_THREE_PASS */
     DS_TILE_OF_COMPACT = 3,        /* compact_if */
     DS_TILE_OF_LDS_TILE_SCAN = 4,  /* ds_tile_scan / ds_tile_pipeline (4-byte types only) */
-    DS_TILE_OF_COUNTING_SORT = 5   /* ds_radix_pass / ds_moe_align: keys per chunk; a workgroup
-                                      takes one to four chunks (4-byte types only) */
+    DS_TILE_OF_COUNTING_SORT = 5   /* ds_radix_pass: keys per chunk; a workgroup takes one or two
+                                      chunks (4-byte types only; ds_moe_align's chunks are half
+                                      as long) */
 } ds_tile_of;
 
 /*

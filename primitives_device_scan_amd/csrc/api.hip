@@ -409,7 +409,7 @@ int ds_moe_align(const int32_t* d_topk_ids, int64_t n, int num_experts, int bloc
         for (int j = i + 1; j < 4; ++j)
             if (ptrs[i] && ptrs[j] && overlaps(ptrs[i], sizes[i], ptrs[j], sizes[j])) return DS_ERR_OVERLAP;
     }
-    const int64_t tiles = n > 0 ? (n + ds::sort_tile_elems(n) - 1) / ds::sort_tile_elems(n) : 0;
+    const int64_t tiles = n > 0 ? (n + ds::moe_tile_elems(n) - 1) / ds::moe_tile_elems(n) : 0;
     const int64_t words = (int64_t)num_experts * tiles;
     std::lock_guard<std::mutex> lock(g_mu);
     char* aux = nullptr;

@@ -6,7 +6,7 @@
 // token dispatch" and exercise 2).
 //
 // Three launches, reduce-then-scan style:
-//   1. digit_count_kernel: each tile (one to four chunks of 4,096 keys)
+//   1. digit_count_kernel: each tile (one or two chunks of keys)
 //      counts its digits in LDS and writes count[d * tiles + tile] -- a
 //      digit-major table;
 //   2. the device-wide exclusive scan of that table (the look-back scan): the
@@ -29,9 +29,12 @@
 
 namespace ds {
 
-constexpr int kSortItems = 16;                        // keys per lane per chunk
-constexpr int kSortChunk = kThreads * kSortItems;     // 4,096 keys
-constexpr int kSortMaxChunks = 4;                     // chunks per tile, at most
+// Keys per lane per chunk (a chunk is kThreads * ITEMS keys): larger chunks
+// give longer runs per digit and fewer barriers per key for the radix pass;
+// MoE inputs are small, and smaller chunks give more workgroups.
+constexpr int kRadixItems = 32;                       // 8,192-key chunks
+constexpr int kMoeItems = 16;                         // 4,096-id chunks
+constexpr int kSortMaxChunks = 2;                     // chunks per tile, at most
 constexpr int kSortMaxBuckets = 512;                  // real buckets + the spare one
 
 struct RadixDigit {
@@ -181,38 +184,37 @@ __device__ __forceinline__ int64_t xcd_contiguous_tile()
     return (int64_t)(x * q + (x < r ? x : r) + b / 8u);
 }
 
-// LDS of a workgroup that ranks and scatters 4,096-key chunks.
-template <int VALS>
+// LDS of a workgroup that ranks and scatters chunks of kThreads * ITEMS keys.
+template <int VALS, int ITEMS>
 struct SortLds {
     uint32_t cnt[kWaves][kSortMaxBuckets];  // per wave: running count, then staging base
     uint32_t gbase[kSortMaxBuckets];        // next output slot of each bucket
     uint32_t gdelta[kSortMaxBuckets];       // output slot - staging position, this chunk
-    uint32_t stage_k[kSortChunk];
-    uint32_t stage_v[VALS ? kSortChunk : 1];
+    uint32_t stage_k[kThreads * ITEMS];
+    uint32_t stage_v[VALS ? kThreads * ITEMS : 1];
     uint32_t s_wave[kWaves];
     uint32_t s_real;
 };
 
-// This wave's 1,024 keys of the chunk at `chunk`, in input order: slot s of
+// This wave's 64 * ITEMS keys of the chunk at `chunk`, in input order: slot s of
 // lane l is element s*64 + l of the wave's segment. All loads are issued
 // before any is used. Returns whether the whole segment lies below n.
-template <int VALS>
+template <int VALS, int ITEMS>
 __device__ __forceinline__ bool load_chunk(const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in,
-                                           int64_t n, int64_t chunk, uint32_t (&key)[kSortItems],
-                                           uint32_t (&val)[kSortItems])
+                                           int64_t n, int64_t chunk, uint32_t (&key)[ITEMS], uint32_t (&val)[ITEMS])
 {
     const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
-    const int64_t seg = chunk + (int64_t)wave * (kWave * kSortItems);
-    const bool whole = seg + kWave * kSortItems <= n;
+    const int64_t seg = chunk + (int64_t)wave * (kWave * ITEMS);
+    const bool whole = seg + kWave * ITEMS <= n;
     if (whole) {
 #pragma unroll
-        for (int s = 0; s < kSortItems; ++s) {
+        for (int s = 0; s < ITEMS; ++s) {
             key[s] = keys[seg + s * kWave + lane];
             if constexpr (VALS == 1) val[s] = vals_in[seg + s * kWave + lane];
         }
     } else {
 #pragma unroll
-        for (int s = 0; s < kSortItems; ++s) {
+        for (int s = 0; s < ITEMS; ++s) {
             const int64_t i = seg + s * kWave + lane;
             key[s] = i < n ? keys[i] : 0u;
             if constexpr (VALS == 1) val[s] = i < n ? vals_in[i] : 0u;
@@ -225,15 +227,15 @@ __device__ __forceinline__ bool load_chunk(const uint32_t* __restrict__ keys, co
 // it, packed with its bucket as (bucket << 16) | rank; `cnt` (this wave's
 // per-bucket counts, zero on entry) ends as the wave's bucket counts. WHOLE:
 // every key of the wave's segment lies below n.
-template <typename DIG, int VALS, int BITS, bool WHOLE>
-__device__ __forceinline__ void rank_in_wave(uint32_t* cnt, const uint32_t (&key)[kSortItems],
-                                             uint32_t (&val)[kSortItems], uint32_t (&dr)[kSortItems], int64_t seg,
+template <typename DIG, int VALS, int BITS, bool WHOLE, int ITEMS>
+__device__ __forceinline__ void rank_in_wave(uint32_t* cnt, const uint32_t (&key)[ITEMS], uint32_t (&val)[ITEMS],
+                                             uint32_t (&dr)[ITEMS], int64_t seg,
                                              int64_t n, DIG dig)
 {
     const uint32_t B = dig.buckets;
     const int lane = lane_id();
 #pragma unroll
-    for (int s = 0; s < kSortItems; ++s) {
+    for (int s = 0; s < ITEMS; ++s) {
         const int64_t i = seg + s * kWave + lane;
         if constexpr (VALS == 2) val[s] = (uint32_t)i;
         const uint32_t d = (WHOLE || i < n) ? dig(key[s]) : B;
@@ -250,30 +252,30 @@ __device__ __forceinline__ void rank_in_wave(uint32_t* cnt, const uint32_t (&key
 // One loaded chunk starting at `chunk` (< n): rank, stage, write; gbase must
 // hold each bucket's next output slot and is advanced past the chunk's keys.
 // Every thread of the workgroup calls it.
-template <typename DIG, int VALS, int BITS>
-__device__ __forceinline__ void rank_and_scatter(SortLds<VALS>& sh, const uint32_t (&key)[kSortItems],
-                                                 uint32_t (&val)[kSortItems], bool whole,
+template <typename DIG, int VALS, int BITS, int ITEMS>
+__device__ __forceinline__ void rank_and_scatter(SortLds<VALS, ITEMS>& sh, const uint32_t (&key)[ITEMS],
+                                                 uint32_t (&val)[ITEMS], bool whole,
                                                  uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
                                                  int64_t n, DIG dig, int64_t chunk, int64_t out_cap)
 {
     const uint32_t B = dig.buckets;  // real buckets; B itself is the spare one
     const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
-    const int64_t seg = chunk + (int64_t)wave * (kWave * kSortItems);
+    const int64_t seg = chunk + (int64_t)wave * (kWave * ITEMS);
     for (uint32_t d = lane; d <= B; d += kWave) sh.cnt[wave][d] = 0;
-    uint32_t dr[kSortItems];
+    uint32_t dr[ITEMS];
     // Rank among this wave's keys of the same bucket, in input order.
     if (whole)
-        rank_in_wave<DIG, VALS, BITS, true>(sh.cnt[wave], key, val, dr, seg, n, dig);
+        rank_in_wave<DIG, VALS, BITS, true, ITEMS>(sh.cnt[wave], key, val, dr, seg, n, dig);
     else
-        rank_in_wave<DIG, VALS, BITS, false>(sh.cnt[wave], key, val, dr, seg, n, dig);
+        rank_in_wave<DIG, VALS, BITS, false, ITEMS>(sh.cnt[wave], key, val, dr, seg, n, dig);
     __syncthreads();
     chunk_bases(sh.cnt, sh.gbase, sh.gdelta, sh.s_wave, &sh.s_real, B);
     __syncthreads();
     // Stage the chunk ordered by bucket, equal buckets in input order.
 #pragma unroll
-    for (int s = 0; s < kSortItems; ++s) {
+    for (int s = 0; s < ITEMS; ++s) {
         const uint32_t p = sh.cnt[wave][dr[s] >> 16] + (dr[s] & 0xFFFFu);
-        if (p < (uint32_t)kSortChunk) {
+        if (p < (uint32_t)(kThreads * ITEMS)) {
             sh.stage_k[p] = key[s];
             if constexpr (VALS != 0) sh.stage_v[p] = val[s];
         }
@@ -341,13 +343,13 @@ __device__ __forceinline__ void moe_bases(uint32_t* gbase, uint32_t* s_wave, con
     }
 }
 
-template <typename DIG, int VALS, int BITS>
+template <typename DIG, int VALS, int BITS, int ITEMS>
 __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, int64_t n, DIG dig, int chunks, const uint32_t* __restrict__ slots,
     MoeSlots moe, int64_t tiles, int64_t out_cap)
 {
-    __shared__ SortLds<VALS> sh;
+    __shared__ SortLds<VALS, ITEMS> sh;
     const int64_t tile = xcd_contiguous_tile();
     if (moe.hist) {
         moe_bases(sh.gbase, sh.s_wave, slots, tiles, tile, dig.buckets, moe, n);
@@ -356,11 +358,11 @@ __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
     }
     __syncthreads();
     for (int c = 0; c < chunks; ++c) {
-        const int64_t chunk = (tile * chunks + c) * (int64_t)kSortChunk;
+        const int64_t chunk = (tile * chunks + c) * (int64_t)(kThreads * ITEMS);
         if (chunk >= n) break;  // uniform over the workgroup
-        uint32_t key[kSortItems], val[kSortItems];
-        const bool whole = load_chunk<VALS>(keys, vals_in, n, chunk, key, val);
-        rank_and_scatter<DIG, VALS, BITS>(sh, key, val, whole, keys_out, vals_out, n, dig, chunk, out_cap);
+        uint32_t key[ITEMS], val[ITEMS];
+        const bool whole = load_chunk<VALS, ITEMS>(keys, vals_in, n, chunk, key, val);
+        rank_and_scatter<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, keys_out, vals_out, n, dig, chunk, out_cap);
     }
 }
 
@@ -458,23 +460,23 @@ __global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(co
     }
 }
 
-// Chunks per tile: four for large inputs (fewer table entries), fewer when
+// Chunks per tile: two for large inputs (half the table entries), one when
 // that would leave the GPU with under ~2,048 workgroups.
-static int chunks_for(int64_t n)
+static int chunks_for(int64_t n, int chunk)
 {
-    const int64_t chunks = (n + kSortChunk - 1) / kSortChunk;
+    const int64_t chunks = (n + chunk - 1) / chunk;
     int c = (int)(chunks / 2048);
     return c < 1 ? 1 : c > kSortMaxChunks ? kSortMaxChunks : c;
 }
 
-template <typename DIG, int VALS>
+template <typename DIG, int VALS, int ITEMS>
 static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out,
                                       uint32_t* vals_out, int64_t n, DIG dig, uint32_t* hist, uint32_t* slots,
                                       const MoeSlots& moe, int64_t out_cap, const DevWs& ws, uint32_t spin_limit,
                                       hipStream_t st)
 {
-    const int chunks = chunks_for(n);
-    const int tile_elems = chunks * kSortChunk;
+    const int chunks = chunks_for(n, kThreads * ITEMS);
+    const int tile_elems = chunks * kThreads * ITEMS;
     const int64_t tiles = (n + tile_elems - 1) / tile_elems;
     const dim3 grid((unsigned)tiles), block(kThreads);
     if (aligned16(keys))
@@ -487,7 +489,7 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
     if (e != hipSuccess) return e;
     const int bits = dig.buckets > 1 ? 32 - __builtin_clz(dig.buckets - 1) : 0;
 #define DS_SCATTER(BITS)                                                                                      \
-    digit_scatter_kernel<DIG, VALS, BITS><<<grid, block, 0, st>>>(keys, vals_in, keys_out, vals_out, n, dig, chunks, \
+    digit_scatter_kernel<DIG, VALS, BITS, ITEMS><<<grid, block, 0, st>>>(keys, vals_in, keys_out, vals_out, n, dig, chunks, \
                                                                   slots, moe, tiles, out_cap);                \
     break
     switch (bits) {
@@ -507,9 +509,10 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
     return hipGetLastError();
 }
 
-int64_t sort_chunk_elems() { return kSortChunk; }
+int64_t sort_chunk_elems() { return kThreads * kRadixItems; }
 int64_t moe_one_launch_max() { return kMoeOneLaunchMax; }
-int64_t sort_tile_elems(int64_t n) { return (int64_t)chunks_for(n) * kSortChunk; }
+int64_t sort_tile_elems(int64_t n) { return (int64_t)chunks_for(n, kThreads * kRadixItems) * kThreads * kRadixItems; }
+int64_t moe_tile_elems(int64_t n) { return (int64_t)chunks_for(n, kThreads * kMoeItems) * kThreads * kMoeItems; }
 int sort_max_buckets() { return kSortMaxBuckets - 1; }
 
 hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out, uint32_t* vals_out,
@@ -521,9 +524,9 @@ hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint
     const RadixDigit dig{(uint32_t)shift, (1u << bits) - 1u, 1u << bits};
     const MoeSlots none{nullptr, 0, nullptr, nullptr, nullptr};
     if (vals_in)
-        return counting_sort_typed<RadixDigit, 1>(keys, vals_in, keys_out, vals_out, n, dig, table, table, none, n, ws,
+        return counting_sort_typed<RadixDigit, 1, kRadixItems>(keys, vals_in, keys_out, vals_out, n, dig, table, table, none, n, ws,
                                                   spin_limit, stream);
-    return counting_sort_typed<RadixDigit, 0>(keys, nullptr, keys_out, nullptr, n, dig, table, table, none, n, ws,
+    return counting_sort_typed<RadixDigit, 0, kRadixItems>(keys, nullptr, keys_out, nullptr, n, dig, table, table, none, n, ws,
                                               spin_limit, stream);
 }
 
@@ -555,7 +558,7 @@ hipError_t launch_moe_align(const int32_t* ids, int64_t n, int experts, const Mo
         return hipGetLastError();
     }
     const MoeSlots moe{hist, out.block, out.counts, out.offsets, out.sorted};
-    return counting_sort_typed<ExpertDigit, 2>((const uint32_t*)ids, nullptr, nullptr, (uint32_t*)out.sorted, n, dig,
+    return counting_sort_typed<ExpertDigit, 2, kMoeItems>((const uint32_t*)ids, nullptr, nullptr, (uint32_t*)out.sorted, n, dig,
                                                hist, slots, moe, out.capacity, ws, spin_limit, stream);
 }
 

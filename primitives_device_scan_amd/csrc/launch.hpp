@@ -43,7 +43,8 @@ hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t st
 // buckets a pass can have.
 int64_t sort_chunk_elems();
 int64_t moe_one_launch_max();  // MoE inputs up to this many ids take one single-workgroup launch
-int64_t sort_tile_elems(int64_t n);
+int64_t sort_tile_elems(int64_t n);  // radix pass
+int64_t moe_tile_elems(int64_t n);   // MoE alignment
 int sort_max_buckets();
 
 // table: (1 << bits) * tiles 32-bit words of scratch (the digit-major counts,

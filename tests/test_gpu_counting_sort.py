@@ -78,9 +78,10 @@ def test_radix_pass_skewed_digits():
         check_radix(keys, 0, 8, np.arange(n, dtype=np.uint32), name)
 
 
-@pytest.mark.parametrize("n", [20_000_003, 30_000_001])
-def test_radix_pass_two_and_three_chunk_tiles(n):
-    # workgroups take one to four 4,096-key chunks depending on n: these sizes take two and three
+@pytest.mark.parametrize("n", [33_546_239, 33_554_433, 40_000_003])
+def test_radix_pass_one_and_two_chunk_tiles(n):
+    # a workgroup takes one 8,192-key chunk below 4,096 chunks of input and two from there on
+    # (the last tile then holding one chunk and a ragged part)
     keys = datagen.keys_u32(n % 1000, n)
     check_radix(keys, 8, 8, None, f"n={n}")
 
