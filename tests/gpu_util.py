@@ -73,24 +73,26 @@ def gpu_scan(x: np.ndarray, inclusive: bool, algo: str = "default", in_place: bo
     return from_dev(out, x.dtype, offset, n)
 
 
-def gpu_compact(x: np.ndarray, op: str, operand, in_place: bool = False):
+def gpu_compact(x: np.ndarray, op: str, operand, in_place: bool = False, offset: int = 0):
+    """compact_if through the C ABI; offset > 0 moves input and output off 16-byte alignment."""
     n = x.size
-    xin = to_dev(x)
+    xin = to_dev(x, extra=offset, offset=offset)
     out = xin if in_place else torch.empty_like(xin)
     if not in_place:
         sentinel_fill(out)
+    esz = x.dtype.itemsize
     cnt = torch.full((1,), -7, dtype=torch.int64, device="cuda")
     bits = ds.operand_bits({np.dtype(np.int32): torch.int32, np.dtype(np.uint32): torch.int64,
                             np.dtype(np.float32): torch.float32, np.dtype(np.int64): torch.int64,
                             np.dtype(np.uint64): torch.int64}[x.dtype], operand)
     if x.dtype == np.uint32:
         bits &= 0xFFFFFFFF
-    st = ds.lib.compact_if(CODE[x.dtype], xin.data_ptr(), out.data_ptr(), cnt.data_ptr(), n, ds.CMP[op], bits,
-                           stream_handle())
+    st = ds.lib.compact_if(CODE[x.dtype], xin.data_ptr() + offset * esz, out.data_ptr() + offset * esz,
+                           cnt.data_ptr(), n, ds.CMP[op], bits, stream_handle())
     assert st == 0, ds.lib.ds_status_string(st)
     torch.cuda.synchronize()
     k = int(cnt.item())
-    return from_dev(out, x.dtype, 0, n), k
+    return from_dev(out, x.dtype, offset, n), k
 
 
 def tile_of(dtype, compact: bool = False, entry: str | None = None) -> int:

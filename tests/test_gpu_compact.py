@@ -67,3 +67,17 @@ def test_compact_all_and_none():
     assert k == n and np.array_equal(out[:k], x)
     out, k = gpu_compact(x, ">", 9)
     assert k == 0
+
+
+@pytest.mark.parametrize("dt", [np.uint32, np.float32, np.int64])
+def test_compact_misaligned(dt):
+    # one element off 16-byte alignment: the element-wise load path
+    T = tile_of(dt, compact=True)
+    case = [c for c in pins.COMPACT_CASES if c[0] == dt][0]
+    for n in (T - 1, 5 * T + 3):
+        x = case[1](910 + n, n).astype(dt)
+        c = case[2][1]
+        out, k = gpu_compact(x, ">", c, offset=1)
+        want = oracle.compact(x, ">", c)
+        assert k == want.size
+        assert_int_equal(out[:k].view(want.dtype), want, f"{np.dtype(dt).name} n={n} misaligned")

@@ -18,9 +18,9 @@ pytestmark = pytest.mark.gpu
 CLAIMS = ("wave", "workgroup")
 
 
-def gpu_compact_unordered(x: np.ndarray, op: str, operand, claim: str):
+def gpu_compact_unordered(x: np.ndarray, op: str, operand, claim: str, offset: int = 0):
     n = x.size
-    xin = to_dev(x)
+    xin = to_dev(x, extra=offset, offset=offset)[offset:]
     out = torch.empty_like(xin)
     sentinel_fill(out)
     cnt = torch.full((1,), -7, dtype=torch.int64, device="cuda")
@@ -113,3 +113,12 @@ def test_unordered_binding():
     k = int(cnt.item())
     assert k == want.size
     assert_int_equal(np.sort(out[:k].cpu().numpy()), np.sort(want), "binding")
+
+
+@pytest.mark.parametrize("claim", CLAIMS)
+def test_unordered_misaligned(claim):
+    T = tile_of(np.uint32, compact=True)
+    n = 7 * T + 13
+    x = datagen.keys_u32(55, n)
+    got, k = gpu_compact_unordered(x, "<", 1 << 30, claim, offset=1)
+    check_multiset(got, k, oracle.compact(x, "<", 1 << 30), f"misaligned claim per {claim}")

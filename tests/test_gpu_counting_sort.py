@@ -23,9 +23,9 @@ def sort_tile():
     return SORT_TILE
 
 
-def gpu_radix_pass(keys: np.ndarray, shift: int, bits: int, vals: np.ndarray | None = None):
+def gpu_radix_pass(keys: np.ndarray, shift: int, bits: int, vals: np.ndarray | None = None, offset: int = 0):
     n = keys.size
-    kin = to_dev(keys)
+    kin = to_dev(keys, extra=offset, offset=offset)[offset:]
     kout = torch.empty(max(n, 1) + 64, dtype=torch.int32, device="cuda")
     sentinel_fill(kout)
     vin = vout = None
@@ -66,6 +66,16 @@ def test_radix_pass_sizes(shift, bits):
         vals = datagen.keys_u32(2000 + n, n)
         check_radix(keys, shift, bits, vals, f"n={n} shift={shift} bits={bits}")
         check_radix(keys, shift, bits, None, f"n={n} shift={shift} bits={bits} keys only")
+
+
+def test_radix_pass_misaligned_keys():
+    # keys one element off 16-byte alignment: the count kernel's element-wise path
+    T = sort_tile()
+    for n in (T + 5, 9 * T + 77):
+        keys = datagen.keys_u32(33 + n, n)
+        ko, _ = gpu_radix_pass(keys, 0, 8, None, offset=1)
+        wk, _ = oracle.radix_pass(keys, 0, 8)
+        assert_int_equal(ko, wk, f"n={n} misaligned keys")
 
 
 def test_radix_pass_skewed_digits():
