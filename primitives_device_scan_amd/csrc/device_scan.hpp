@@ -9,18 +9,26 @@
 namespace ds {
 
 // 16-byte vectors per thread (VPT); a tile is 256 threads x VPT x 16 B.
-//  - look-back scan: the largest tile that fits 4 waves per SIMD without
-//    spilling (ScanVPT below), since resident tile bytes per CU are what hide
-//    the look-back latency (several microseconds under full HBM load) behind
-//    other tiles' transfers: 96 KiB for int32 exclusive, less where the
-//    arithmetic needs more registers (fp32, inclusive, 8-byte);
+//  - look-back scan: the largest tile that fits its occupancy (ScanOcc
+//    below) without spilling (ScanVPT), since resident tile bytes per CU are
+//    what hide the look-back latency (several microseconds under full HBM
+//    load) behind other tiles' transfers: 96 KiB for int32 and fp32
+//    exclusive, 80 KiB inclusive, 80 / 64 KiB for 8-byte types;
 //  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
 //    wait to hide; compaction's keep mask holds 64 elements).
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
-    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 12 : 16)
-                               : __is_same(T, float) ? (INCLUSIVE ? 16 : 20)
+    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 16 : 20)
+                               : __is_same(T, float) ? (INCLUSIVE ? 20 : 24)
                                                      : (INCLUSIVE ? 20 : 24);
+};
+// Workgroups per CU the look-back kernel is compiled for (waves per SIMD):
+// 4 for 4-byte integers (their tiles fit 128 VGPRs); fp32 and 8-byte scans
+// need more registers per vector and hold larger tiles at 3 (measured: 1-2%
+// faster for fp32, 5-6% for 8-byte than their 4-wave tiles).
+template <typename T>
+struct ScanOcc {
+    static constexpr int value = (sizeof(T) == 8 || __is_same(T, float)) ? 3 : 4;
 };
 constexpr int kVPT = 24;  // largest scan tile: the same-pattern copy uses it
 constexpr int kThreePassVPT = 16;
