@@ -236,8 +236,9 @@ int ds_set_spin_limit(uint32_t polls);
 
 /* Which entry point's tile ds_tile_elems reports. */
 typedef enum {
-    DS_TILE_OF_SCAN_EXCLUSIVE = 0, /* scan_exclusive, ds_scan look-back exclusive */
-    DS_TILE_OF_SCAN_INCLUSIVE = 1, /* scan_inclusive, ds_scan look-back inclusive */
+    DS_TILE_OF_SCAN_EXCLUSIVE = 0, /* scan_exclusive, ds_scan look-back exclusive: the tile of
+                                      inputs over 32 MiB (ds_scan_tile_elems for any n) */
+    DS_TILE_OF_SCAN_INCLUSIVE = 1, /* scan_inclusive, ds_scan look-back inclusive: same */
     DS_TILE_OF_THREE_PASS = 2,     /* DS_ALGO_THREE_PASS */
     DS_TILE_OF_COMPACT = 3,        /* compact_if */
     DS_TILE_OF_LDS_TILE_SCAN = 4,  /* ds_tile_scan / ds_tile_pipeline (4-byte types only) */
@@ -252,6 +253,15 @@ typedef enum {
  * tests that aim at tile boundaries. Returns -1 for an invalid dtype or entry.
  */
 int64_t ds_tile_elems(int dtype, int entry);
+
+/*
+ * Elements per workgroup tile of the look-back scan (scan_exclusive,
+ * scan_inclusive, ds_scan look-back) for an input of n elements of `dtype`:
+ * 8 sixteen-byte vectors per thread up to 8 MiB of data, 12 up to 32 MiB,
+ * the type's large tile beyond (so mid-size inputs still spread over many
+ * workgroups). `inclusive` 0 or 1. Returns -1 for invalid arguments.
+ */
+int64_t ds_scan_tile_elems(int dtype, int inclusive, int64_t n);
 
 /* Human-readable name of a ds_status value (static storage). */
 const char* ds_status_string(int status);

@@ -23,7 +23,7 @@ DS_OK = 0
 
 EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_compact_unordered", "ds_radix_pass",
            "ds_moe_align", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
-           "ds_tile_elems", "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace",
+           "ds_tile_elems", "ds_scan_tile_elems", "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace",
            "ds_version"]
 TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4,
            "counting_sort": 5}
@@ -65,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ds_release_workspace.restype = None
     L.ds_tile_elems.argtypes = [I, I]
     L.ds_tile_elems.restype = I64
+    L.ds_scan_tile_elems.argtypes = [I, I, I64]
+    L.ds_scan_tile_elems.restype = I64
     L.ds_version.argtypes = []
     L.ds_version.restype = I
     return L

@@ -123,7 +123,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 // (none when it fits one tile).
 int scan_workspace_u32(hipStream_t stream, int64_t words, DevWs* dws, Workspace** w)
 {
-    const int64_t te = ds::tile_elems(ds::kU32, false);
+    const int64_t te = ds::tile_elems(ds::kU32, false, words);
     const int64_t tiles = (words + te - 1) / te;
     *dws = DevWs{nullptr, nullptr, nullptr};
     *w = nullptr;
@@ -176,7 +176,7 @@ int scan_impl(int dtype, int inclusive, int algo, const void* in, void* out, int
     // three-pass call on one tile runs the look-back kernel instead.
     const int64_t tp = ds::three_pass_tile_elems(elem_bytes(dtype));
     const bool three = algo == DS_ALGO_THREE_PASS && n > tp;
-    const int64_t te = three ? tp : ds::tile_elems(kind_of(dtype), inclusive != 0);
+    const int64_t te = three ? tp : ds::tile_elems(kind_of(dtype), inclusive != 0, n);
     const int64_t tiles = (n + te - 1) / te;
     std::lock_guard<std::mutex> lock(g_mu);
     DevWs dws{nullptr, nullptr, nullptr};
@@ -444,14 +444,20 @@ int64_t ds_tile_elems(int dtype, int entry)
     if (!valid_dtype(dtype)) return -1;
     const int b = elem_bytes(dtype);
     switch (entry) {
-    case DS_TILE_OF_SCAN_EXCLUSIVE: return ds::tile_elems(kind_of(dtype), false);
-    case DS_TILE_OF_SCAN_INCLUSIVE: return ds::tile_elems(kind_of(dtype), true);
+    case DS_TILE_OF_SCAN_EXCLUSIVE: return ds::tile_elems(kind_of(dtype), false, INT64_MAX / 16);
+    case DS_TILE_OF_SCAN_INCLUSIVE: return ds::tile_elems(kind_of(dtype), true, INT64_MAX / 16);
     case DS_TILE_OF_THREE_PASS: return ds::three_pass_tile_elems(b);
     case DS_TILE_OF_COMPACT: return ds::compact_tile_elems(b);
     case DS_TILE_OF_LDS_TILE_SCAN: return b == 4 ? ds::lds_tile_elems() : -1;
     case DS_TILE_OF_COUNTING_SORT: return b == 4 ? ds::sort_chunk_elems() : -1;
     default: return -1;
     }
+}
+
+int64_t ds_scan_tile_elems(int dtype, int inclusive, int64_t n)
+{
+    if (!valid_dtype(dtype) || (inclusive != 0 && inclusive != 1) || n < 0) return -1;
+    return ds::tile_elems(kind_of(dtype), inclusive != 0, n);
 }
 
 int ds_version(void) { return 1; }

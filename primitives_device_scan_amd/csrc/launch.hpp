@@ -18,7 +18,7 @@ struct DevWs {
 
 enum ElemKind { kU32 = 0, kF32 = 1, kU64 = 2, kI32 = 3, kI64 = 4 };
 
-int64_t tile_elems(ElemKind kind, bool inclusive);  // look-back scan tile
+int64_t tile_elems(ElemKind kind, bool inclusive, int64_t n);  // look-back scan tile for n elements
 int64_t three_pass_tile_elems(int elem_bytes);  // three-pass scan tile
 int64_t compact_tile_elems(int elem_bytes);     // compaction tile
 int64_t tile_bytes();

@@ -42,16 +42,45 @@ __global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_ker
         store_scalar<T, VPT>(out, seg, n, lane, e);
 }
 
-template <typename T, bool INCL, bool VEC>
-static hipError_t lookback_typed(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
-                                 hipStream_t st)
+// Vectors per thread for n elements: the per-type large tile (ScanVPT) from
+// 32 MiB of data on, where resident bytes must hide the look-back; below, a
+// large tile would leave most CUs idle (1M int32 fill 41 workgroups of 96 KiB)
+// and a small last tile costs element-wise loads, so mid-size inputs take 12
+// vectors per thread and inputs up to 8 MiB take 8 (measured: one 4,096-int32
+// tile 7.9 -> 3.8 us, 1M int32 10.0 -> 5.6 us, 8M int32 14.5 -> 13.5 us per
+// launch back to back; from 30M on the large tile is fastest).
+constexpr int kSmallScanVPT = 8;
+constexpr int kMidScanVPT = 12;
+
+template <typename T, bool INCL>
+static int lookback_vpt(int64_t n)
 {
-    constexpr int VPT = ScanVPT<T, INCL>::value;
+    const int64_t bytes = n * (int64_t)sizeof(T);
+    if (bytes <= ((int64_t)8 << 20)) return kSmallScanVPT;
+    if (bytes <= ((int64_t)32 << 20)) return kMidScanVPT;
+    return ScanVPT<T, INCL>::value;
+}
+
+template <typename T, bool INCL, bool VEC, int VPT>
+static hipError_t lookback_launch(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
+                                  hipStream_t st)
+{
     const int64_t tiles = (n + Shape<T, VPT>::kTile - 1) / Shape<T, VPT>::kTile;
     if (tiles > 1 && (!ws.ctrl || !ws.status)) return hipErrorInvalidValue;  // several tiles need a workspace
     lookback_scan_kernel<T, INCL, VEC, VPT><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
         (const T*)in, (T*)out, n, tiles, ws.ctrl, ws.status, spin);
     return hipGetLastError();
+}
+
+template <typename T, bool INCL, bool VEC>
+static hipError_t lookback_typed(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
+                                 hipStream_t st)
+{
+    switch (lookback_vpt<T, INCL>(n)) {
+    case kSmallScanVPT: return lookback_launch<T, INCL, VEC, kSmallScanVPT>(in, out, n, ws, spin, st);
+    case kMidScanVPT: return lookback_launch<T, INCL, VEC, kMidScanVPT>(in, out, n, ws, spin, st);
+    default: return lookback_launch<T, INCL, VEC, ScanVPT<T, INCL>::value>(in, out, n, ws, spin, st);
+    }
 }
 
 template <typename T>
@@ -77,16 +106,20 @@ hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, v
     }
 }
 
-int64_t tile_elems(ElemKind kind, bool inclusive)
+template <typename T>
+static int64_t tile_of(bool inclusive, int64_t n)
+{
+    const int vpt = inclusive ? lookback_vpt<T, true>(n) : lookback_vpt<T, false>(n);
+    return (int64_t)kThreads * vpt * (kVecBytes / (int)sizeof(T));
+}
+
+int64_t tile_elems(ElemKind kind, bool inclusive, int64_t n)
 {
     switch (kind) {
-    case kF32: return inclusive ? Shape<float, ScanVPT<float, true>::value>::kTile
-                                : Shape<float, ScanVPT<float, false>::value>::kTile;
+    case kF32: return tile_of<float>(inclusive, n);
     case kU64:
-    case kI64: return inclusive ? Shape<uint64_t, ScanVPT<uint64_t, true>::value>::kTile
-                                : Shape<uint64_t, ScanVPT<uint64_t, false>::value>::kTile;
-    default: return inclusive ? Shape<uint32_t, ScanVPT<uint32_t, true>::value>::kTile
-                              : Shape<uint32_t, ScanVPT<uint32_t, false>::value>::kTile;
+    case kI64: return tile_of<uint64_t>(inclusive, n);
+    default: return tile_of<uint32_t>(inclusive, n);
     }
 }
 

@@ -104,6 +104,11 @@ def tile_of(dtype, compact: bool = False, entry: str | None = None) -> int:
     return int(ds.lib.ds_tile_elems(CODE[np.dtype(dtype)], ds._binding.TILE_OF[entry]))
 
 
+def scan_tile(dtype, inclusive: bool, n: int) -> int:
+    """Elements per look-back tile for an input of n elements (ds_scan_tile_elems)."""
+    return int(ds.lib.ds_scan_tile_elems(CODE[np.dtype(dtype)], int(inclusive), n))
+
+
 def assert_int_equal(got: np.ndarray, want: np.ndarray, what: str):
     if got.shape == want.shape and np.array_equal(got, want):
         return

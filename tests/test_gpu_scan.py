@@ -11,7 +11,8 @@ import torch
 import datagen
 import oracle
 import pins
-from gpu_util import (assert_fp32_close, assert_int_equal, cached_workload, check_scan, gpu_scan, say, tile_of)
+from gpu_util import (assert_fp32_close, assert_int_equal, cached_workload, check_scan, gpu_scan, say, scan_tile,
+                      tile_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +46,7 @@ def test_worked_examples(dt, algo):
 
 def test_one_tile_int32_exclusive():
     x = cached_workload("one_tile")
-    assert x.size <= tile_of(np.int32)  # one workgroup, no look-back
+    assert x.size <= scan_tile(np.int32, False, x.size)  # one workgroup, no look-back
     say("one_tile int32 exclusive n=4096 (single workgroup)")
     check_scan(x, False, gpu_scan(x, False), "one_tile")
     check_scan(x, False, gpu_scan(x, False, entry="scan_exclusive"), "one_tile via scan_exclusive")
@@ -123,6 +124,26 @@ def test_edge_sizes(dt, algo):
         x = _input(dt, n, 1000 + n)
         for inc in (False, True):
             check_scan(x, inc, gpu_scan(x, inc, algo), f"{np.dtype(dt).name} n={n} inc={inc} {algo}")
+
+
+def _regime_sizes(dt, inc):
+    """Sizes at the tile boundaries of each look-back tile regime (8 vectors per thread up to
+    8 MiB of data, 12 up to 32 MiB, the large tile beyond) and at the regime boundaries."""
+    esz = np.dtype(dt).itemsize
+    small_max, mid_max = (8 << 20) // esz, (32 << 20) // esz
+    ts, tm, tl = scan_tile(dt, inc, 1), scan_tile(dt, inc, small_max + 1), scan_tile(dt, inc, mid_max + 1)
+    assert ts < tm < tl or (ts < tm and tl >= tm), (ts, tm, tl)
+    km, kl = small_max // tm + 2, mid_max // tl + 1
+    return [ts - 1, ts, ts + 1, 7 * ts + 3, small_max, small_max + 1, km * tm - 1, km * tm, km * tm + 1,
+            mid_max, mid_max + 1, kl * tl - 1, kl * tl, kl * tl + 1]
+
+
+@pytest.mark.parametrize("dt", [np.int32, np.float32, np.int64], ids=lambda d: np.dtype(d).name)
+def test_tile_regimes(dt):
+    for inc in (False, True):
+        for n in _regime_sizes(dt, inc):
+            x = _input(dt, n, 3000 + n % 997)
+            check_scan(x, inc, gpu_scan(x, inc), f"{np.dtype(dt).name} n={n} inc={inc} tile {scan_tile(dt, inc, n)}")
 
 
 def test_wraparound():
@@ -232,8 +253,9 @@ def test_three_pass_on_one_tile_runs_the_lookback_kernel(dt):
     three-pass tile runs the look-back kernel, whose tiles can be smaller
     (a regression test for a workspace that was sized by the wrong tile)."""
     sizes = set()
-    for entry in ("scan_exclusive", "scan_inclusive", "three_pass"):
-        t = tile_of(dt, entry=entry)
+    tiles = [tile_of(dt, entry=entry) for entry in ("scan_exclusive", "scan_inclusive", "three_pass")]
+    tiles += [scan_tile(dt, inc, 1) for inc in (False, True)]  # the look-back tile of small inputs
+    for t in tiles:
         sizes |= {t - 1, t, t + 1, 2 * t - 1, 2 * t + 1}
     for n in sorted(sizes):
         x = _input(dt, n, 5000 + n)
