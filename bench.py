@@ -13,7 +13,9 @@ seeded (datagen). Prints one JSON line:
              HIP events on the launch stream
   cpu_baseline  the sequential CPU oracle on the host, same inputs
   extras     the same-pattern copy, the three-pass scan, cold-cache scans,
-             and (unless --no-compact / --no-sort) compaction of 268,435,456
+             the other workloads' scans (one tile, 1M int32, fp32 10M
+             inclusive, int64 100M), and (unless --no-compact / --no-sort)
+             compaction of 268,435,456
              uint32 keys (ordered and both unordered forms), one 8-bit
              counting-sort pass over those keys (with and without values) and
              MoE alignment of two router workloads
@@ -334,6 +336,30 @@ def main():
     tp_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 0, ds.ALGO["three_pass"], d_xi.data_ptr(), d_yi.data_ptr(), n, sh))
     extras["three_pass_int32_gelem_s"] = round(n / (tp_ms * 1e-3) / 1e9, 2)
     extras["three_pass_int32_alg_gbs"] = round(alg_bytes / (tp_ms * 1e-3) / 1e9, 1)
+    # inclusive at the headline size, reusing its buffers
+    ii_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 1, 0, d_xi.data_ptr(), d_yi.data_ptr(), n, sh))
+    extras["int32_incl_100m_us"] = round(ii_ms * 1e3, 1)
+    del d_xf, d_yf
+
+    # the other workloads' configurations, each as its own launch (median of 20)
+    def config_time(x_np, dcode, incl):
+        dx = torch.from_numpy(x_np).to(dev)
+        dy = torch.empty_like(dx)
+        ms = timed(lambda: L.ds_scan(dcode, incl, 0, dx.data_ptr(), dy.data_ptr(), x_np.size, sh))
+        return ms, dx.numel() * dx.element_size() * 2
+    for name, dcode, incl in (("one_tile", ds.DS_INT32, 0), ("mid", ds.DS_INT32, 0), ("mid", ds.DS_INT32, 1),
+                              ("fp32_10m", ds.DS_FP32, 1)):
+        ms, nbytes = config_time(datagen.workload(name), dcode, incl)
+        key = f"{name}_{'incl' if incl else 'excl'}"
+        extras[f"{key}_us"] = round(ms * 1e3, 2)
+        extras[f"{key}_alg_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    x64 = datagen.uniform_i64(64, n, 40)
+    for incl in (0, 1):
+        ms, nbytes = config_time(x64, ds.DS_INT64, incl)
+        key = f"int64_100m_{'incl' if incl else 'excl'}"
+        extras[f"{key}_us"] = round(ms * 1e3, 1)
+        extras[f"{key}_alg_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del x64
 
     if not args.no_compact:
         nk = datagen.WORKLOADS["compact_256m"][0]
