@@ -11,7 +11,9 @@ seeded (datagen). Prints one JSON line:
   roofline   the look-back scan kernel against MI355X peak HBM bandwidth:
              algorithmic bytes 2 * n * 4 per launch / mean launch time from
              HIP events on the launch stream
-  cpu_baseline  the sequential CPU oracle on the host, same inputs
+  cpu_baseline  the sequential CPU oracle on the host, same inputs (extras
+             also carry a second CPU row: a two-pass blocked scan on up to
+             16 host threads)
   extras     the same-pattern copy, the three-pass scan, cold-cache scans,
              the other workloads' scans (one tile, 1M int32, fp32 10M
              inclusive, int64 100M), and (unless --no-compact / --no-sort)
@@ -430,6 +432,25 @@ def main():
         cpu = {"value": round(2.0 * n * reps / t_cpu / 1e9, 4), "unit": "G-elem/s", "cores": 1, "kind": "oracle",
                "sample": f"{reps} full steps (int32 + fp32 exclusive scans of n={n}), sequential C, "
                          f"{t_cpu:.1f} s on {os.cpu_count()} visible host cores, 1 used"}
+        # Second CPU row: the two-pass blocked scan on host threads (reads the
+        # input twice), the same full step, median of a few.
+        par = oracle.ParallelScan()
+        thr = oracle.host_threads()
+        yf32 = np.empty_like(x_f)
+        par.scan(x_i, False, thr, out=yi)  # untimed: touches the output pages
+        par.scan(x_f, False, thr, out=yf32)
+        steps_par = []
+        while sum(steps_par) < 3.0 and len(steps_par) < 20:
+            c0 = time.perf_counter()
+            par.scan(x_i, False, thr, out=yi)
+            par.scan(x_f, False, thr, out=yf32)
+            steps_par.append(time.perf_counter() - c0)
+        t_par = float(np.median(steps_par))
+        extras["cpu_parallel_baseline"] = {
+            "value": round(2.0 * n / t_par / 1e9, 4), "unit": "G-elem/s", "cores": thr,
+            "kind": "two-pass blocked scan, one block per thread (pthreads)",
+            "sample": f"median of {len(steps_par)} full steps (int32 + fp32 exclusive scans of n={n})"}
+        del yi, yf, sf, yf32
 
     traffic = measured_traffic(alg_bytes)
     out = {

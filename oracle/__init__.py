@@ -17,6 +17,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+PAR_SRC = os.path.join(HERE, "parallel_scan.c")
+PAR_LIB = os.path.join(HERE, "libparallel_scan.so")
 
 OPS = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
 
@@ -25,11 +27,17 @@ _I64 = ctypes.c_int64
 
 
 def build(src: str = SRC, out: str = LIB) -> str:
-    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    """Compile the oracle with gcc (no fast-math, no FP contraction); with the
+    default paths, also the threaded CPU comparison scan."""
     tmp = out + ".tmp"
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
                     "-fno-fast-math", "-o", tmp, src], check=True)
     os.replace(tmp, out)
+    if src == SRC and out == LIB:
+        tmp = PAR_LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
+                        "-fno-fast-math", "-o", tmp, PAR_SRC], check=True)
+        os.replace(tmp, PAR_LIB)
     return out
 
 
@@ -116,6 +124,44 @@ class Oracle:
                                           offsets.ctypes.data, srt.ctypes.data, cap)
         assert total >= 0
         return counts, offsets, srt[:total]
+
+
+class ParallelScan:
+    """The two-pass blocked scan on host threads (``parallel_scan.c``): a CPU
+    comparison row for the benchmark, checked against the oracle, never used
+    as one."""
+
+    def __init__(self, path: str = PAR_LIB):
+        if not os.path.exists(path):
+            build()
+        self.lib = ctypes.CDLL(path)
+        for name in ("par_scan_u32", "par_scan_f32"):
+            getattr(self.lib, name).argtypes = [_P, _P, _I64, ctypes.c_int, ctypes.c_int]
+            getattr(self.lib, name).restype = ctypes.c_int
+
+    def scan(self, x: np.ndarray, inclusive: bool, threads: int, out: np.ndarray | None = None) -> np.ndarray:
+        """int32/uint32 (wrapping) or fp32 (fp64 accumulation, fp32 result) scan of x, in x's dtype."""
+        x = np.ascontiguousarray(x)
+        y = np.empty_like(x) if out is None else out
+        assert y.dtype == x.dtype and y.size == x.size and y.flags.c_contiguous
+        if x.dtype in (np.int32, np.uint32):
+            rc = self.lib.par_scan_u32(x.ctypes.data, y.ctypes.data, x.size, int(inclusive), threads)
+        elif x.dtype == np.float32:
+            rc = self.lib.par_scan_f32(x.ctypes.data, y.ctypes.data, x.size, int(inclusive), threads)
+        else:
+            raise TypeError(f"unsupported dtype {x.dtype}")
+        if rc != 0:
+            raise RuntimeError("parallel_scan: could not start its threads")
+        return y
+
+
+def host_threads() -> int:
+    """Cores this process may run on, capped at 16 (a one-GPU share of a host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 _default: Oracle | None = None
