@@ -37,16 +37,25 @@ constexpr int kMoeItems = 16;                         // 4,096-id chunks
 constexpr int kSortMaxChunks = 2;                     // chunks per tile, at most
 constexpr int kSortMaxBuckets = 512;                  // real buckets + the spare one
 
+// digit<BITS>(k) is the same bucket as operator(), BITS = ceil(log2(buckets))
+// known at compile time. kSpareKeys: whether a key itself can fall in the
+// spare bucket (else only the ragged end of the last chunk goes there).
 struct RadixDigit {
-    uint32_t shift, mask, buckets;
+    uint32_t shift, mask, buckets;  // buckets = 2^BITS, mask = buckets - 1
+    static constexpr bool kSpareKeys = false;
     __device__ __forceinline__ uint32_t operator()(uint32_t k) const { return (k >> shift) & mask; }
+    template <int BITS>
+    __device__ __forceinline__ uint32_t digit(uint32_t k) const { return __builtin_amdgcn_ubfe(k, shift, BITS); }
 };
 
 // Expert ids: an id outside [0, experts) (negative ones included, as unsigned)
 // goes to the spare bucket.
 struct ExpertDigit {
     uint32_t buckets;
+    static constexpr bool kSpareKeys = true;
     __device__ __forceinline__ uint32_t operator()(uint32_t k) const { return k < buckets ? k : buckets; }
+    template <int BITS>
+    __device__ __forceinline__ uint32_t digit(uint32_t k) const { return k < buckets ? k : buckets; }
 };
 
 __device__ __forceinline__ uint32_t lanes_below_mask(uint64_t mask)
@@ -54,25 +63,50 @@ __device__ __forceinline__ uint32_t lanes_below_mask(uint64_t mask)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Lanes whose bucket equals this lane's: one ballot per bit of the real
-// bucket indices (a lane differs from another where their bits' ballots
-// disagree), the spare bucket told apart by a ballot of its own. Every lane
-// of the wave takes part.
-template <int BITS>
+// Lanes whose bucket equals this lane's. For every bit b of the real bucket
+// indices, the wave's ballot of that bit is kept where this lane has the bit
+// and complemented where it does not, and the results are ANDed:
+// same &= ~(ballot_b ^ mine_b), with mine_b = bit b of d copied into all 32
+// bits -- one three-input bitwise op (v_bitop3, truth table 0x90 for
+// s0 & ~(s1 ^ s2)) per 32-lane half, so a bit costs four VALU instructions.
+// SPARE: some lane may hold the spare bucket, whose lanes match only each
+// other (its low bits can equal a real bucket's). Every lane of the wave
+// takes part.
+template <int BITS, bool SPARE>
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, uint32_t spare)
 {
-    const bool is_spare = d == spare;
-    const uint64_t spare_lanes = ballot(is_spare);
-    uint32_t lo = (uint32_t)spare_lanes, hi = (uint32_t)(spare_lanes >> 32);
+    constexpr unsigned kKeepWhereEqual = 0x90;
+    constexpr int kIcmpNe = 33;  // the "not equal" integer predicate of the lane-mask compare
+    uint32_t lo = ~0u, hi = ~0u;
 #pragma unroll
     for (int b = 0; b < BITS; ++b) {
-        const int32_t mine = __builtin_amdgcn_sbfe((int32_t)d, b, 1);  // 0, or all ones where bit b is set
-        const uint64_t set = ballot(mine != 0);
-        lo |= (uint32_t)set ^ (uint32_t)mine;
-        hi |= (uint32_t)(set >> 32) ^ (uint32_t)mine;
+        const uint32_t mine = (uint32_t)__builtin_amdgcn_sbfe((int32_t)d, b, 1);  // 0 or all ones
+        const uint64_t set = __builtin_amdgcn_uicmp(mine, 0u, kIcmpNe);         // lanes with bit b
+        lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)set, mine, kKeepWhereEqual);
+        hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(set >> 32), mine, kKeepWhereEqual);
     }
-    const uint64_t same = ~(((uint64_t)hi << 32) | lo);
-    return is_spare ? spare_lanes : same;
+    const uint64_t same = ((uint64_t)hi << 32) | lo;
+    if constexpr (!SPARE) {
+        return same;
+    } else {
+        const bool is_spare = d == spare;
+        const uint64_t spare_lanes = ballot(is_spare);
+        return is_spare ? spare_lanes : (same & ~spare_lanes);
+    }
+}
+
+// Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b mod 8).
+// Renumbering them so that each XCD takes a contiguous run of tiles puts
+// neighbouring tiles, which write neighbouring words, on the same XCD, whose
+// L2 then merges their partial cache lines before they go to HBM: the count
+// table's entries (d, tile) and (d, tile + 1), and the two halves of the line
+// at each bucket's run boundary in the scatter. Any order of tiles is correct
+// in both kernels: a tile's table column and its output slots follow from
+// its number alone.
+__device__ __forceinline__ int64_t xcd_contiguous_tile()
+{
+    const uint32_t G = gridDim.x, b = blockIdx.x, x = b % 8u, q = G / 8u, r = G % 8u;
+    return (int64_t)(x * q + (x < r ? x : r) + b / 8u);
 }
 
 template <typename DIG, bool VEC>
@@ -85,7 +119,8 @@ __global__ __launch_bounds__(kThreads) void digit_count_kernel(const uint32_t* _
     const int wave = (int)(threadIdx.x / kWave);
     for (uint32_t i = threadIdx.x; i < kWaves * kSortMaxBuckets; i += kThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * tile_elems;
+    const int64_t tile = xcd_contiguous_tile();
+    const int64_t base = tile * tile_elems;
     if (VEC && base + tile_elems <= n) {
         const u32x4* p = reinterpret_cast<const u32x4*>(keys + base);
 #pragma unroll 4
@@ -109,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void digit_count_kernel(const uint32_t* _
         uint32_t c = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) c += hist[w][d];
-        table[(int64_t)d * tiles + blockIdx.x] = c;
+        table[(int64_t)d * tiles + tile] = c;
     }
 }
 
@@ -173,17 +208,6 @@ __device__ __forceinline__ void chunk_bases(uint32_t (*cnt)[kSortMaxBuckets], ui
     }
 }
 
-// Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b mod 8).
-// Renumbering them so that each XCD takes a contiguous run of tiles puts the
-// two tiles that share a partly written cache line at each bucket's run
-// boundary on the same XCD, whose L2 then merges the two halves. Any order of
-// tiles is correct here: a tile's output slots come from the scanned table.
-__device__ __forceinline__ int64_t xcd_contiguous_tile()
-{
-    const uint32_t G = gridDim.x, b = blockIdx.x, x = b % 8u, q = G / 8u, r = G % 8u;
-    return (int64_t)(x * q + (x < r ? x : r) + b / 8u);
-}
-
 // LDS of a workgroup that ranks and scatters chunks of kThreads * ITEMS keys.
 template <int VALS, int ITEMS>
 struct SortLds {
@@ -232,14 +256,15 @@ __device__ __forceinline__ void rank_in_wave(uint32_t* cnt, const uint32_t (&key
                                              uint32_t (&dr)[ITEMS], int64_t seg,
                                              int64_t n, DIG dig)
 {
+    constexpr bool kSpare = !WHOLE || DIG::kSpareKeys;
     const uint32_t B = dig.buckets;
     const int lane = lane_id();
 #pragma unroll
     for (int s = 0; s < ITEMS; ++s) {
         const int64_t i = seg + s * kWave + lane;
         if constexpr (VALS == 2) val[s] = (uint32_t)i;
-        const uint32_t d = (WHOLE || i < n) ? dig(key[s]) : B;
-        const uint64_t peers = match_digit<BITS>(d, B);
+        const uint32_t d = (WHOLE || i < n) ? dig.template digit<BITS>(key[s]) : B;
+        const uint64_t peers = match_digit<BITS, kSpare>(d, B);
         const uint32_t below = lanes_below_mask(peers);
         const uint32_t run = cnt[d];
         if (below == 0) cnt[d] = run + (uint32_t)__builtin_popcountll(peers);
@@ -249,14 +274,15 @@ __device__ __forceinline__ void rank_in_wave(uint32_t* cnt, const uint32_t (&key
 
 // VALS: 0 keys only; 1 values from vals_in follow the keys; 2 the value is the
 // element's index and only values are written (MoE: the assignment index).
-// One loaded chunk starting at `chunk` (< n): rank, stage, write; gbase must
-// hold each bucket's next output slot and is advanced past the chunk's keys.
-// Every thread of the workgroup calls it.
+// One loaded chunk starting at `chunk` (< n): rank, then stage it in LDS
+// ordered by bucket; gbase must hold each bucket's next output slot and is
+// advanced past the chunk's keys, gdelta maps staging positions to output
+// slots. Every thread of the workgroup calls it; ends with a barrier, after
+// which key and val are free.
 template <typename DIG, int VALS, int BITS, int ITEMS>
-__device__ __forceinline__ void rank_and_scatter(SortLds<VALS, ITEMS>& sh, const uint32_t (&key)[ITEMS],
-                                                 uint32_t (&val)[ITEMS], bool whole,
-                                                 uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
-                                                 int64_t n, DIG dig, int64_t chunk, int64_t out_cap)
+__device__ __forceinline__ void rank_and_stage(SortLds<VALS, ITEMS>& sh, const uint32_t (&key)[ITEMS],
+                                               uint32_t (&val)[ITEMS], bool whole, int64_t n, DIG dig,
+                                               int64_t chunk)
 {
     const uint32_t B = dig.buckets;  // real buckets; B itself is the spare one
     const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
@@ -281,12 +307,21 @@ __device__ __forceinline__ void rank_and_scatter(SortLds<VALS, ITEMS>& sh, const
         }
     }
     __syncthreads();
-    // Each bucket's run goes to its slots; the spare bucket's keys, staged
-    // last, are not written.
+}
+
+// Each bucket's run of the staged chunk goes to its slots; the spare
+// bucket's keys, staged last, are not written. Reads only stage_k, stage_v,
+// gdelta and s_real, which the next rank_and_stage rewrites only after its
+// first barrier.
+template <typename DIG, int VALS, int BITS, int ITEMS>
+__device__ __forceinline__ void write_runs(const SortLds<VALS, ITEMS>& sh, uint32_t* __restrict__ keys_out,
+                                           uint32_t* __restrict__ vals_out, DIG dig, int64_t out_cap)
+{
+    const uint32_t B = dig.buckets;
     const uint32_t real = sh.s_real;
     for (uint32_t j = threadIdx.x; j < real; j += kThreads) {
         const uint32_t k = sh.stage_k[j];
-        const uint32_t d = dig(k);
+        const uint32_t d = dig.template digit<BITS>(k);
         const uint64_t pos = (uint64_t)(uint32_t)(sh.gdelta[d] + j);
         if (d < B && pos < (uint64_t)out_cap) {
             if constexpr (VALS != 2) keys_out[pos] = k;
@@ -357,12 +392,20 @@ __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
         for (uint32_t d = threadIdx.x; d < dig.buckets; d += kThreads) sh.gbase[d] = slots[(int64_t)d * tiles + tile];
     }
     __syncthreads();
+    // The next chunk's keys are loaded before this chunk's runs are written,
+    // so their latency overlaps the stores instead of following them.
+    const int64_t first = tile * chunks * (int64_t)(kThreads * ITEMS);
+    if (first >= n) return;  // uniform over the workgroup
+    uint32_t key[ITEMS], val[ITEMS];
+    bool whole = load_chunk<VALS, ITEMS>(keys, vals_in, n, first, key, val);
     for (int c = 0; c < chunks; ++c) {
-        const int64_t chunk = (tile * chunks + c) * (int64_t)(kThreads * ITEMS);
-        if (chunk >= n) break;  // uniform over the workgroup
-        uint32_t key[ITEMS], val[ITEMS];
-        const bool whole = load_chunk<VALS, ITEMS>(keys, vals_in, n, chunk, key, val);
-        rank_and_scatter<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, keys_out, vals_out, n, dig, chunk, out_cap);
+        const int64_t chunk = first + c * (int64_t)(kThreads * ITEMS);
+        rank_and_stage<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, n, dig, chunk);
+        const int64_t next = chunk + kThreads * ITEMS;
+        const bool more = c + 1 < chunks && next < n;  // uniform over the workgroup
+        if (more) whole = load_chunk<VALS, ITEMS>(keys, vals_in, n, next, key, val);
+        write_runs<DIG, VALS, BITS, ITEMS>(sh, keys_out, vals_out, dig, out_cap);
+        if (!more) break;
     }
 }
 
@@ -408,7 +451,7 @@ __global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(co
         if (s < slots) {  // uniform
             const int64_t i = seg + s * kWave + lane;
             const uint32_t d = i < n ? dig(key[s]) : E;
-            const uint64_t peers = match_digit<BITS>(d, E);
+            const uint64_t peers = match_digit<BITS, true>(d, E);
             const uint32_t below = lanes_below_mask(peers);
             const uint32_t run = cnt[wave][d];
             if (below == 0) cnt[wave][d] = run + (uint32_t)__builtin_popcountll(peers);
