@@ -161,7 +161,9 @@ int ds_compact_unordered(int dtype, const void* d_in, void* d_out, int64_t* d_nu
  * memory. 1 <= bits <= 8, 0 <= shift,
  * shift + bits <= 32 (else DS_ERR_INVALID_VALUE); n < 2^32 (else
  * DS_ERR_TOO_LARGE). Scratch: 2^bits x (number of tiles) words, a tile being
- * 8,192 or 16,384 keys; cached per (device, stream) like the scan workspace.
+ * ds_tile_elems(DS_UINT32, DS_TILE_OF_COUNTING_SORT) keys, or
+ * DS_TILE_OF_COUNTING_SORT_VALUES with values; cached per (device, stream)
+ * like the scan workspace.
  */
 int ds_radix_pass(const uint32_t* d_keys_in, uint32_t* d_keys_out, const uint32_t* d_vals_in,
                   uint32_t* d_vals_out, int64_t n, int shift, int bits, hipStream_t stream);
@@ -176,8 +178,10 @@ int ds_radix_pass(const uint32_t* d_keys_in, uint32_t* d_keys_out, const uint32_
  * index i (into d_topk_ids) of expert e's j-th assignment in input order, the
  * rest of expert e's segment = n (the padding mark). Entries of d_sorted_ids
  * from d_offsets[num_experts] on are not written. The same counting-sort
- * pass as ds_radix_pass with the expert id as the digit, plus a one-workgroup
- * launch for the rounded offsets. 1 <= num_experts <= 511, block >= 1,
+ * pass as ds_radix_pass with the expert id as the digit (tiles of
+ * ds_tile_elems(DS_INT32, DS_TILE_OF_MOE_ALIGN) ids), each scatter workgroup
+ * deriving the rounded offsets from the scanned table; up to 8,192 ids, one
+ * launch of one workgroup does all of it. 1 <= num_experts <= 511, block >= 1,
  * capacity >= n + num_experts * (block - 1) (else DS_ERR_INVALID_VALUE); that
  * bound < 2^31 (else DS_ERR_TOO_LARGE). Buffers must not overlap.
  */
@@ -242,9 +246,9 @@ typedef enum {
     DS_TILE_OF_THREE_PASS = 2,     /* DS_ALGO_THREE_PASS */
     DS_TILE_OF_COMPACT = 3,        /* compact_if */
     DS_TILE_OF_LDS_TILE_SCAN = 4,  /* ds_tile_scan / ds_tile_pipeline (4-byte types only) */
-    DS_TILE_OF_COUNTING_SORT = 5   /* ds_radix_pass: keys per chunk; a workgroup takes one or two
-                                      chunks (4-byte types only; ds_moe_align's chunks are half
-                                      as long) */
+    DS_TILE_OF_COUNTING_SORT = 5,  /* ds_radix_pass without values (4-byte types only) */
+    DS_TILE_OF_COUNTING_SORT_VALUES = 6, /* ds_radix_pass with values (4-byte types only) */
+    DS_TILE_OF_MOE_ALIGN = 7       /* ds_moe_align above its one-launch size (4-byte types only) */
 } ds_tile_of;
 
 /*

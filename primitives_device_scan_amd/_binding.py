@@ -26,7 +26,7 @@ EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_comp
            "ds_tile_elems", "ds_scan_tile_elems", "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace",
            "ds_version"]
 TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4,
-           "counting_sort": 5}
+           "counting_sort": 5, "counting_sort_values": 6, "moe_align": 7}
 TILE_VARIANTS = {"tree": 0, "tree_pad1": 1, "tree_pad2": 2, "hillis_steele": 3}
 
 

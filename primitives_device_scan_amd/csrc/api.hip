@@ -377,7 +377,8 @@ int ds_radix_pass(const uint32_t* d_keys_in, uint32_t* d_keys_out, const uint32_
             if (i == 0 && j == 2) continue;  // the two inputs may share memory: both are only read
             if (ptrs[i] && ptrs[j] && overlaps(ptrs[i], bytes, ptrs[j], bytes)) return DS_ERR_OVERLAP;
         }
-    const int64_t tiles = n > 0 ? (n + ds::sort_tile_elems(n) - 1) / ds::sort_tile_elems(n) : 0;
+    const int64_t tile = ds::sort_tile_elems(d_vals_in != nullptr);
+    const int64_t tiles = (n + tile - 1) / tile;
     const int64_t words = ((int64_t)1 << bits) * tiles;
     std::lock_guard<std::mutex> lock(g_mu);
     char* aux = nullptr;
@@ -409,7 +410,7 @@ int ds_moe_align(const int32_t* d_topk_ids, int64_t n, int num_experts, int bloc
         for (int j = i + 1; j < 4; ++j)
             if (ptrs[i] && ptrs[j] && overlaps(ptrs[i], sizes[i], ptrs[j], sizes[j])) return DS_ERR_OVERLAP;
     }
-    const int64_t tiles = n > 0 ? (n + ds::moe_tile_elems(n) - 1) / ds::moe_tile_elems(n) : 0;
+    const int64_t tiles = (n + ds::moe_tile_elems() - 1) / ds::moe_tile_elems();
     const int64_t words = (int64_t)num_experts * tiles;
     std::lock_guard<std::mutex> lock(g_mu);
     char* aux = nullptr;
@@ -449,7 +450,9 @@ int64_t ds_tile_elems(int dtype, int entry)
     case DS_TILE_OF_THREE_PASS: return ds::three_pass_tile_elems(b);
     case DS_TILE_OF_COMPACT: return ds::compact_tile_elems(b);
     case DS_TILE_OF_LDS_TILE_SCAN: return b == 4 ? ds::lds_tile_elems() : -1;
-    case DS_TILE_OF_COUNTING_SORT: return b == 4 ? ds::sort_chunk_elems() : -1;
+    case DS_TILE_OF_COUNTING_SORT: return b == 4 ? ds::sort_tile_elems(false) : -1;
+    case DS_TILE_OF_COUNTING_SORT_VALUES: return b == 4 ? ds::sort_tile_elems(true) : -1;
+    case DS_TILE_OF_MOE_ALIGN: return b == 4 ? ds::moe_tile_elems() : -1;
     default: return -1;
     }
 }

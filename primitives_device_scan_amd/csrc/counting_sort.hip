@@ -6,9 +6,9 @@
 // token dispatch" and exercise 2).
 //
 // Three launches, reduce-then-scan style:
-//   1. digit_count_kernel: each tile (one or two chunks of keys)
-//      counts its digits in LDS and writes count[d * tiles + tile] -- a
-//      digit-major table;
+//   1. digit_count_kernel: each tile (kThreads * ITEMS keys) counts its
+//      digits in LDS and writes count[d * tiles + tile] -- a digit-major
+//      table;
 //   2. the device-wide exclusive scan of that table (the look-back scan): the
 //      entry (d, tile) becomes the first output slot of tile's digit-d keys;
 //   3. digit_scatter_kernel: each tile ranks its keys in input order -- a
@@ -29,12 +29,15 @@
 
 namespace ds {
 
-// Keys per lane per chunk (a chunk is kThreads * ITEMS keys): larger chunks
-// give longer runs per digit and fewer barriers per key for the radix pass;
-// MoE inputs are small, and smaller chunks give more workgroups.
-constexpr int kRadixItems = 32;                       // 8,192-key chunks
-constexpr int kMoeItems = 16;                         // 4,096-id chunks
-constexpr int kSortMaxChunks = 2;                     // chunks per tile, at most
+// Keys per lane per tile (a tile is kThreads * ITEMS keys). Longer tiles
+// give longer runs per digit, so fewer partly written lines, and fewer
+// barriers per key, until registers and LDS cut the workgroups per CU: the
+// keys-only radix pass holds 24 per lane (4 workgroups per CU), with values
+// 20 (the staged values take LDS too; 3 workgroups per CU); MoE inputs are
+// small, and shorter tiles give more workgroups.
+constexpr int kRadixItems = 24;                       // 6,144-key tiles
+constexpr int kRadixKvItems = 20;                     // 5,120-key tiles
+constexpr int kMoeItems = 8;                          // 2,048-id tiles
 constexpr int kSortMaxBuckets = 512;                  // real buckets + the spare one
 
 // digit<BITS>(k) is the same bucket as operator(), BITS = ceil(log2(buckets))
@@ -208,7 +211,7 @@ __device__ __forceinline__ void chunk_bases(uint32_t (*cnt)[kSortMaxBuckets], ui
     }
 }
 
-// LDS of a workgroup that ranks and scatters chunks of kThreads * ITEMS keys.
+// LDS of a workgroup that ranks and scatters its tile of kThreads * ITEMS keys.
 template <int VALS, int ITEMS>
 struct SortLds {
     uint32_t cnt[kWaves][kSortMaxBuckets];  // per wave: running count, then staging base
@@ -274,11 +277,10 @@ __device__ __forceinline__ void rank_in_wave(uint32_t* cnt, const uint32_t (&key
 
 // VALS: 0 keys only; 1 values from vals_in follow the keys; 2 the value is the
 // element's index and only values are written (MoE: the assignment index).
-// One loaded chunk starting at `chunk` (< n): rank, then stage it in LDS
-// ordered by bucket; gbase must hold each bucket's next output slot and is
-// advanced past the chunk's keys, gdelta maps staging positions to output
-// slots. Every thread of the workgroup calls it; ends with a barrier, after
-// which key and val are free.
+// The tile's loaded chunk of keys starting at `chunk` (< n): rank, then
+// stage it in LDS ordered by bucket; gbase must hold each bucket's first
+// output slot for this tile, and gdelta ends mapping staging positions to
+// output slots. Every thread of the workgroup calls it; ends with a barrier.
 template <typename DIG, int VALS, int BITS, int ITEMS>
 __device__ __forceinline__ void rank_and_stage(SortLds<VALS, ITEMS>& sh, const uint32_t (&key)[ITEMS],
                                                uint32_t (&val)[ITEMS], bool whole, int64_t n, DIG dig,
@@ -310,9 +312,7 @@ __device__ __forceinline__ void rank_and_stage(SortLds<VALS, ITEMS>& sh, const u
 }
 
 // Each bucket's run of the staged chunk goes to its slots; the spare
-// bucket's keys, staged last, are not written. Reads only stage_k, stage_v,
-// gdelta and s_real, which the next rank_and_stage rewrites only after its
-// first barrier.
+// bucket's keys, staged last, are not written.
 template <typename DIG, int VALS, int BITS, int ITEMS>
 __device__ __forceinline__ void write_runs(const SortLds<VALS, ITEMS>& sh, uint32_t* __restrict__ keys_out,
                                            uint32_t* __restrict__ vals_out, DIG dig, int64_t out_cap)
@@ -381,32 +381,25 @@ __device__ __forceinline__ void moe_bases(uint32_t* gbase, uint32_t* s_wave, con
 template <typename DIG, int VALS, int BITS, int ITEMS>
 __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, int64_t n, DIG dig, int chunks, const uint32_t* __restrict__ slots,
-    MoeSlots moe, int64_t tiles, int64_t out_cap)
+    uint32_t* __restrict__ vals_out, int64_t n, DIG dig, const uint32_t* __restrict__ slots, MoeSlots moe,
+    int64_t tiles, int64_t out_cap)
 {
     __shared__ SortLds<VALS, ITEMS> sh;
     const int64_t tile = xcd_contiguous_tile();
+    const int64_t chunk = tile * (int64_t)(kThreads * ITEMS);
+    if (chunk >= n) return;  // uniform over the workgroup
+    // The tile's keys are requested first, so their latency overlaps the
+    // reads of its column of the scanned table.
+    uint32_t key[ITEMS], val[ITEMS];
+    const bool whole = load_chunk<VALS, ITEMS>(keys, vals_in, n, chunk, key, val);
     if (moe.hist) {
         moe_bases(sh.gbase, sh.s_wave, slots, tiles, tile, dig.buckets, moe, n);
     } else {
         for (uint32_t d = threadIdx.x; d < dig.buckets; d += kThreads) sh.gbase[d] = slots[(int64_t)d * tiles + tile];
     }
     __syncthreads();
-    // The next chunk's keys are loaded before this chunk's runs are written,
-    // so their latency overlaps the stores instead of following them.
-    const int64_t first = tile * chunks * (int64_t)(kThreads * ITEMS);
-    if (first >= n) return;  // uniform over the workgroup
-    uint32_t key[ITEMS], val[ITEMS];
-    bool whole = load_chunk<VALS, ITEMS>(keys, vals_in, n, first, key, val);
-    for (int c = 0; c < chunks; ++c) {
-        const int64_t chunk = first + c * (int64_t)(kThreads * ITEMS);
-        rank_and_stage<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, n, dig, chunk);
-        const int64_t next = chunk + kThreads * ITEMS;
-        const bool more = c + 1 < chunks && next < n;  // uniform over the workgroup
-        if (more) whole = load_chunk<VALS, ITEMS>(keys, vals_in, n, next, key, val);
-        write_runs<DIG, VALS, BITS, ITEMS>(sh, keys_out, vals_out, dig, out_cap);
-        if (!more) break;
-    }
+    rank_and_stage<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, n, dig, chunk);
+    write_runs<DIG, VALS, BITS, ITEMS>(sh, keys_out, vals_out, dig, out_cap);
 }
 
 // MoE alignment of up to kMoeOneLaunchMax ids in one launch of one
@@ -503,23 +496,13 @@ __global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(co
     }
 }
 
-// Chunks per tile: two for large inputs (half the table entries), one when
-// that would leave the GPU with under ~2,048 workgroups.
-static int chunks_for(int64_t n, int chunk)
-{
-    const int64_t chunks = (n + chunk - 1) / chunk;
-    int c = (int)(chunks / 2048);
-    return c < 1 ? 1 : c > kSortMaxChunks ? kSortMaxChunks : c;
-}
-
 template <typename DIG, int VALS, int ITEMS>
 static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out,
                                       uint32_t* vals_out, int64_t n, DIG dig, uint32_t* hist, uint32_t* slots,
                                       const MoeSlots& moe, int64_t out_cap, const DevWs& ws, uint32_t spin_limit,
                                       hipStream_t st)
 {
-    const int chunks = chunks_for(n, kThreads * ITEMS);
-    const int tile_elems = chunks * kThreads * ITEMS;
+    const int tile_elems = kThreads * ITEMS;
     const int64_t tiles = (n + tile_elems - 1) / tile_elems;
     const dim3 grid((unsigned)tiles), block(kThreads);
     if (aligned16(keys))
@@ -532,7 +515,7 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
     if (e != hipSuccess) return e;
     const int bits = dig.buckets > 1 ? 32 - __builtin_clz(dig.buckets - 1) : 0;
 #define DS_SCATTER(BITS)                                                                                      \
-    digit_scatter_kernel<DIG, VALS, BITS, ITEMS><<<grid, block, 0, st>>>(keys, vals_in, keys_out, vals_out, n, dig, chunks, \
+    digit_scatter_kernel<DIG, VALS, BITS, ITEMS><<<grid, block, 0, st>>>(keys, vals_in, keys_out, vals_out, n, dig,         \
                                                                   slots, moe, tiles, out_cap);                \
     break
     switch (bits) {
@@ -552,10 +535,10 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
     return hipGetLastError();
 }
 
-int64_t sort_chunk_elems() { return kThreads * kRadixItems; }
+
 int64_t moe_one_launch_max() { return kMoeOneLaunchMax; }
-int64_t sort_tile_elems(int64_t n) { return (int64_t)chunks_for(n, kThreads * kRadixItems) * kThreads * kRadixItems; }
-int64_t moe_tile_elems(int64_t n) { return (int64_t)chunks_for(n, kThreads * kMoeItems) * kThreads * kMoeItems; }
+int64_t sort_tile_elems(bool values) { return (int64_t)kThreads * (values ? kRadixKvItems : kRadixItems); }
+int64_t moe_tile_elems() { return (int64_t)kThreads * kMoeItems; }
 int sort_max_buckets() { return kSortMaxBuckets - 1; }
 
 hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out, uint32_t* vals_out,
@@ -567,7 +550,7 @@ hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint
     const RadixDigit dig{(uint32_t)shift, (1u << bits) - 1u, 1u << bits};
     const MoeSlots none{nullptr, 0, nullptr, nullptr, nullptr};
     if (vals_in)
-        return counting_sort_typed<RadixDigit, 1, kRadixItems>(keys, vals_in, keys_out, vals_out, n, dig, table, table, none, n, ws,
+        return counting_sort_typed<RadixDigit, 1, kRadixKvItems>(keys, vals_in, keys_out, vals_out, n, dig, table, table, none, n, ws,
                                                   spin_limit, stream);
     return counting_sort_typed<RadixDigit, 0, kRadixItems>(keys, nullptr, keys_out, nullptr, n, dig, table, table, none, n, ws,
                                               spin_limit, stream);

@@ -38,13 +38,11 @@ hipError_t launch_compact_unordered(ElemKind kind, const void* in, void* out, in
 
 hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t stream);
 
-// Counting-sort pass (radix sort step, MoE alignment): keys per chunk, keys
-// per workgroup tile for n keys (one to four chunks), and the most real
-// buckets a pass can have.
-int64_t sort_chunk_elems();
-int64_t moe_one_launch_max();  // MoE inputs up to this many ids take one single-workgroup launch
-int64_t sort_tile_elems(int64_t n);  // radix pass
-int64_t moe_tile_elems(int64_t n);   // MoE alignment
+// Counting-sort pass (radix sort step, MoE alignment): keys per workgroup
+// tile, and the most real buckets a pass can have.
+int64_t moe_one_launch_max();          // MoE inputs up to this many ids take one single-workgroup launch
+int64_t sort_tile_elems(bool values);  // radix pass, keys only or with values
+int64_t moe_tile_elems();              // MoE alignment
 int sort_max_buckets();
 
 // table: (1 << bits) * tiles 32-bit words of scratch (the digit-major counts,

@@ -153,6 +153,24 @@ def test_copy_validation(lib):
     assert lib.ds_copy(A, A + 16, 64, None) == 3
 
 
+def test_tile_queries(lib):
+    from primitives_device_scan_amd import _binding
+    # host-only queries: every tile is whole waves of a 256-thread workgroup;
+    # the counting-sort tiles exist for 4-byte keys only
+    for entry in _binding.TILE_OF.values():
+        t = lib.ds_tile_elems(1, entry)
+        assert t > 0 and t % 256 == 0, (entry, t)
+    for name in ("counting_sort", "counting_sort_values", "moe_align", "lds_tile_scan"):
+        assert lib.ds_tile_elems(3, _binding.TILE_OF[name]) == -1, name
+    assert lib.ds_tile_elems(1, max(_binding.TILE_OF.values()) + 1) == -1
+    assert lib.ds_tile_elems(1, -1) == -1
+    assert lib.ds_tile_elems(9, 0) == -1
+    for n in (0, 1, 4096, 1 << 20, 1 << 23, 100_000_007):
+        t = lib.ds_scan_tile_elems(1, 0, n)
+        assert t > 0 and t % 256 == 0, (n, t)
+    assert lib.ds_scan_tile_elems(1, 2, 10) == -1 and lib.ds_scan_tile_elems(1, 0, -1) == -1
+
+
 def test_query_timeout_null(lib):
     assert lib.ds_query_timeout(None, None) == 1
 

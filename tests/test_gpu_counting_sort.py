@@ -13,14 +13,15 @@ from gpu_util import assert_int_equal, cached_workload, from_dev, say, sentinel_
 
 pytestmark = pytest.mark.gpu
 
-SORT_TILE = None
+_TILES = {}
 
 
-def sort_tile():
-    global SORT_TILE
-    if SORT_TILE is None:
-        SORT_TILE = int(ds.lib.ds_tile_elems(1, ds._binding.TILE_OF["counting_sort"]))
-    return SORT_TILE
+def sort_tile(entry: str = "counting_sort") -> int:
+    """Keys per workgroup tile of the radix pass ("counting_sort", or with values
+    "counting_sort_values") or of multi-launch MoE alignment ("moe_align")."""
+    if entry not in _TILES:
+        _TILES[entry] = int(ds.lib.ds_tile_elems(1, ds._binding.TILE_OF[entry]))
+    return _TILES[entry]
 
 
 def gpu_radix_pass(keys: np.ndarray, shift: int, bits: int, vals: np.ndarray | None = None, offset: int = 0):
@@ -58,14 +59,27 @@ def check_radix(keys, shift, bits, vals, what):
 DIGITS = [(0, 8), (8, 8), (24, 8), (28, 4), (31, 1), (5, 3)]
 
 
+def around_tiles(T: int):
+    return (1, 7, 64, 4095, 4096, 4097, T - 1, T, T + 1, 3 * T + 5, 70 * T + 3)
+
+
 @pytest.mark.parametrize("shift,bits", DIGITS)
 def test_radix_pass_sizes(shift, bits):
-    T = sort_tile()
-    for n in (1, 7, 64, 4095, 4096, 4097, T - 1, T, T + 1, 3 * T + 5, 70 * T + 3):
+    # sizes around the tile of each form: keys only, and keys with values
+    for n in around_tiles(sort_tile("counting_sort")):
+        keys = datagen.keys_u32(1000 + n, n)
+        check_radix(keys, shift, bits, None, f"n={n} shift={shift} bits={bits} keys only")
+    for n in around_tiles(sort_tile("counting_sort_values")):
         keys = datagen.keys_u32(1000 + n, n)
         vals = datagen.keys_u32(2000 + n, n)
         check_radix(keys, shift, bits, vals, f"n={n} shift={shift} bits={bits}")
-        check_radix(keys, shift, bits, None, f"n={n} shift={shift} bits={bits} keys only")
+
+
+def test_tiles_are_whole_waves():
+    # every lane of a tile's four waves holds the same number of keys
+    for entry in ("counting_sort", "counting_sort_values", "moe_align"):
+        T = sort_tile(entry)
+        assert T > 0 and T % 256 == 0, (entry, T)
 
 
 def test_radix_pass_misaligned_keys():
@@ -89,11 +103,11 @@ def test_radix_pass_skewed_digits():
 
 
 @pytest.mark.parametrize("n", [33_546_239, 33_554_433, 40_000_003])
-def test_radix_pass_one_and_two_chunk_tiles(n):
-    # a workgroup takes one 8,192-key chunk below 4,096 chunks of input and two from there on
-    # (the last tile then holding one chunk and a ragged part)
+def test_radix_pass_large_ragged(n):
+    # thousands of tiles, the last one ragged; keys only and with values
     keys = datagen.keys_u32(n % 1000, n)
     check_radix(keys, 8, 8, None, f"n={n}")
+    check_radix(keys, 16, 8, np.arange(n, dtype=np.uint32), f"n={n} with values")
 
 
 def test_radix_pass_256m_keys():
@@ -155,8 +169,9 @@ def test_moe_workloads(name):
 @pytest.mark.parametrize("experts,top_k,block", [(1, 1, 1), (8, 2, 16), (64, 6, 64), (256, 8, 128), (511, 8, 32),
                                                   (100, 3, 7)])
 def test_moe_shapes(experts, top_k, block):
-    T = sort_tile()
-    for tokens in (1, 5, 1000, T // top_k + 1, 3 * T // top_k + 11):
+    T = sort_tile("moe_align")
+    # one-launch sizes (up to 8,192 ids), then past the one-launch size by about one and three tiles
+    for tokens in (1, 5, 1000, (8192 + T) // top_k + 1, (8192 + 3 * T) // top_k + 11):
         ids = datagen.moe_topk_ids(70 + tokens, tokens, top_k, experts)
         check_moe(ids, experts, block, f"E={experts} k={top_k} block={block} tokens={tokens}")
 
