@@ -422,12 +422,12 @@ __global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(co
                                                                              int32_t* __restrict__ sorted)
 {
     __shared__ uint32_t cnt[kMoeWaves][kSortMaxBuckets];
-    __shared__ uint32_t s_count[kSortMaxBuckets], s_off[kSortMaxBuckets];
+    __shared__ uint32_t s_count[kSortMaxBuckets], s_off[kSortMaxBuckets], s_round[kSortMaxBuckets];
     __shared__ uint32_t s_wave[kMoeWaves];
     const uint32_t E = dig.buckets;
     const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
-    for (uint32_t i = threadIdx.x; i < kMoeWaves * kSortMaxBuckets; i += kMoeThreadsOne) (&cnt[0][0])[i] = 0;
     // Wave w's segment: seg_len ids from w * seg_len, seg_len a multiple of 64.
+    // The ids are requested first; the counters are cleared while they load.
     const int64_t seg_len = (n + kMoeThreadsOne - 1) / kMoeThreadsOne * kWave;
     const int slots = (int)(seg_len / kWave);
     const int64_t seg = (int64_t)wave * seg_len;
@@ -437,6 +437,7 @@ __global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(co
         const int64_t i = seg + s * kWave + lane;
         key[s] = (s < slots && i < n) ? ids[i] : 0u;
     }
+    for (uint32_t i = threadIdx.x; i < kMoeWaves * kSortMaxBuckets; i += kMoeThreadsOne) (&cnt[0][0])[i] = 0;
     __syncthreads();
     uint32_t dr[kMoeSlots];
 #pragma unroll
@@ -477,14 +478,14 @@ __global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(co
         for (int w = 0; w < kMoeWaves; ++w) cnt[w][e] = off + pw[w];
         s_count[e] = c;
         s_off[e] = off;
+        s_round[e] = r;
     }
     if (e == E) offsets[E] = (int32_t)off;  // r = 0 here: the padded total
     __syncthreads();
     // Padding marks: wave w takes experts w, w + 16, ...; its lanes write the
     // unused slots of the expert's rounded segment side by side.
     for (uint32_t x = wave; x < E; x += kMoeWaves) {
-        const uint32_t cx = s_count[x], ox = s_off[x];
-        const uint32_t rx = (cx + block - 1) / block * block;
+        const uint32_t cx = s_count[x], ox = s_off[x], rx = s_round[x];
         for (uint32_t j = cx + lane; j < rx; j += kWave) sorted[ox + j] = (int32_t)n;
     }
 #pragma unroll
