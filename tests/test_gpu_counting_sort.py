@@ -82,6 +82,28 @@ def test_tiles_are_whole_waves():
         assert T > 0 and T % 256 == 0, (entry, T)
 
 
+def test_radix_pass_values_alias_keys():
+    # the two inputs may be one buffer (both are only read): each key carries itself as its value
+    T = sort_tile("counting_sort_values")
+    n = 7 * T + 13
+    keys = datagen.keys_u32(91, n)
+    kin = to_dev(keys)
+    kout = torch.empty(n + 64, dtype=torch.int32, device="cuda")
+    vout = torch.empty(n + 64, dtype=torch.int32, device="cuda")
+    sentinel_fill(kout)
+    sentinel_fill(vout)
+    st = ds.lib.ds_radix_pass(kin.data_ptr(), kout.data_ptr(), kin.data_ptr(), vout.data_ptr(), n, 4, 8,
+                              stream_handle())
+    assert st == 0, ds.lib.ds_status_string(st)
+    torch.cuda.synchronize()
+    wk, wv = oracle.radix_pass(keys, 4, 8, keys)
+    ko, vo = from_dev(kout, np.uint32), from_dev(vout, np.uint32)
+    assert_int_equal(ko[:n], wk, "aliased inputs: keys")
+    assert_int_equal(vo[:n], wv, "aliased inputs: values")
+    assert np.all(ko[n:] == 0xA5A5A5A5) and np.all(vo[n:] == 0xA5A5A5A5), "written past n"
+    assert np.array_equal(from_dev(kin, np.uint32), keys), "input changed"
+
+
 def test_radix_pass_misaligned_keys():
     # keys one element off 16-byte alignment: the count kernel's element-wise path
     T = sort_tile()
