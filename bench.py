@@ -44,6 +44,18 @@ KERNEL_SOURCES = ["primitives_device_scan_amd/csrc/tile.hpp", "primitives_device
                   "primitives_device_scan_amd/csrc/scan_lookback.hip"]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -431,7 +443,8 @@ def main():
             reps += 1
         cpu = {"value": round(2.0 * n * reps / t_cpu / 1e9, 4), "unit": "G-elem/s", "cores": 1, "kind": "oracle",
                "sample": f"{reps} full steps (int32 + fp32 exclusive scans of n={n}), sequential C, "
-                         f"{t_cpu:.1f} s on {os.cpu_count()} visible host cores, 1 used"}
+                         f"{t_cpu:.1f} s on {os.cpu_count()} visible host cores, 1 used",
+               "cpu_model": cpu_model()}
         # Second CPU row: the two-pass blocked scan on host threads (reads the
         # input twice), the same full step, median of a few.
         par = oracle.ParallelScan()
@@ -448,7 +461,7 @@ def main():
         t_par = float(np.median(steps_par))
         extras["cpu_parallel_baseline"] = {
             "value": round(2.0 * n / t_par / 1e9, 4), "unit": "G-elem/s", "cores": thr,
-            "kind": "two-pass blocked scan, one block per thread (pthreads)",
+            "kind": "two-pass blocked scan, one block per thread (pthreads)", "cpu_model": cpu_model(),
             "sample": f"median of {len(steps_par)} full steps (int32 + fp32 exclusive scans of n={n})"}
         del yi, yf, sf, yf32
 
