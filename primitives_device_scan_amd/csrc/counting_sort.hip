@@ -13,16 +13,19 @@
 //      entry (d, tile) becomes the first output slot of tile's digit-d keys;
 //   3. digit_scatter_kernel: each tile ranks its keys in input order -- a
 //      wave matches equal digits with one ballot per digit bit and counts the
-//      matching lanes below each lane -- stages the chunk in LDS ordered by
+//      matching lanes below each lane -- stages the tile in LDS ordered by
 //      digit, and writes each digit's run to its slot, so equal digits keep
 //      their input order (the pass is stable).
+// One tile per workgroup in both kernels: the cache line two neighbouring
+// tiles share at a bucket's run boundary is then written by both at the same
+// stage of their lives and merges in L2 instead of going to HBM twice.
 // For MoE alignment every scatter workgroup also derives the experts' counts
 // and block-rounded offsets from the scanned table and shifts each expert's
 // slots to its padded start (workgroup 0 writes counts, offsets and padding
 // marks); up to kMoeOneLaunchMax ids, one workgroup does all of it in a
 // single launch (moe_align_one_launch_kernel).
 // Bucket B (one past the last real digit) collects elements that belong to
-// no bucket: the ragged end of the last chunk and, for MoE, ids outside
+// no bucket: the ragged end of the last tile and, for MoE, ids outside
 // [0, experts). It takes part in the ranking but is never written.
 #include "device_scan.hpp"
 #include "launch.hpp"
@@ -42,7 +45,7 @@ constexpr int kSortMaxBuckets = 512;                  // real buckets + the spar
 
 // digit<BITS>(k) is the same bucket as operator(), BITS = ceil(log2(buckets))
 // known at compile time. kSpareKeys: whether a key itself can fall in the
-// spare bucket (else only the ragged end of the last chunk goes there).
+// spare bucket (else only the ragged end of the last tile goes there).
 struct RadixDigit {
     uint32_t shift, mask, buckets;  // buckets = 2^BITS, mask = buckets - 1
     static constexpr bool kSpareKeys = false;
@@ -172,9 +175,9 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t* s_
 
 // Buckets d0 = 2t and d1 = 2t + 1 of thread t: the four waves' counts in
 // `cnt` become each wave's first staging position for the bucket; gdelta[d]
-// becomes (output slot of the chunk's first bucket-d key) - (its staging
-// position); gbase[d] moves past this chunk's bucket-d keys.
-__device__ __forceinline__ void chunk_bases(uint32_t (*cnt)[kSortMaxBuckets], uint32_t* gbase, uint32_t* gdelta,
+// becomes (output slot of the tile's first bucket-d key) - (its staging
+// position); gbase[d] moves past this tile's bucket-d keys.
+__device__ __forceinline__ void tile_bases(uint32_t (*cnt)[kSortMaxBuckets], uint32_t* gbase, uint32_t* gdelta,
                                             uint32_t* s_wave, uint32_t* s_real, uint32_t B)
 {
     const uint32_t d0 = 2 * threadIdx.x, d1 = d0 + 1;
@@ -216,22 +219,22 @@ template <int VALS, int ITEMS>
 struct SortLds {
     uint32_t cnt[kWaves][kSortMaxBuckets];  // per wave: running count, then staging base
     uint32_t gbase[kSortMaxBuckets];        // next output slot of each bucket
-    uint32_t gdelta[kSortMaxBuckets];       // output slot - staging position, this chunk
+    uint32_t gdelta[kSortMaxBuckets];       // output slot - staging position
     uint32_t stage_k[kThreads * ITEMS];
     uint32_t stage_v[VALS ? kThreads * ITEMS : 1];
     uint32_t s_wave[kWaves];
     uint32_t s_real;
 };
 
-// This wave's 64 * ITEMS keys of the chunk at `chunk`, in input order: slot s of
+// This wave's 64 * ITEMS keys of the tile starting at `first`, in input order: slot s of
 // lane l is element s*64 + l of the wave's segment. All loads are issued
 // before any is used. Returns whether the whole segment lies below n.
 template <int VALS, int ITEMS>
-__device__ __forceinline__ bool load_chunk(const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in,
-                                           int64_t n, int64_t chunk, uint32_t (&key)[ITEMS], uint32_t (&val)[ITEMS])
+__device__ __forceinline__ bool load_tile(const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in,
+                                          int64_t n, int64_t first, uint32_t (&key)[ITEMS], uint32_t (&val)[ITEMS])
 {
     const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
-    const int64_t seg = chunk + (int64_t)wave * (kWave * ITEMS);
+    const int64_t seg = first + (int64_t)wave * (kWave * ITEMS);
     const bool whole = seg + kWave * ITEMS <= n;
     if (whole) {
 #pragma unroll
@@ -277,18 +280,18 @@ __device__ __forceinline__ void rank_in_wave(uint32_t* cnt, const uint32_t (&key
 
 // VALS: 0 keys only; 1 values from vals_in follow the keys; 2 the value is the
 // element's index and only values are written (MoE: the assignment index).
-// The tile's loaded chunk of keys starting at `chunk` (< n): rank, then
+// The tile's loaded keys, starting at `first` (< n): rank, then
 // stage it in LDS ordered by bucket; gbase must hold each bucket's first
 // output slot for this tile, and gdelta ends mapping staging positions to
 // output slots. Every thread of the workgroup calls it; ends with a barrier.
 template <typename DIG, int VALS, int BITS, int ITEMS>
 __device__ __forceinline__ void rank_and_stage(SortLds<VALS, ITEMS>& sh, const uint32_t (&key)[ITEMS],
                                                uint32_t (&val)[ITEMS], bool whole, int64_t n, DIG dig,
-                                               int64_t chunk)
+                                               int64_t first)
 {
     const uint32_t B = dig.buckets;  // real buckets; B itself is the spare one
     const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
-    const int64_t seg = chunk + (int64_t)wave * (kWave * ITEMS);
+    const int64_t seg = first + (int64_t)wave * (kWave * ITEMS);
     for (uint32_t d = lane; d <= B; d += kWave) sh.cnt[wave][d] = 0;
     uint32_t dr[ITEMS];
     // Rank among this wave's keys of the same bucket, in input order.
@@ -297,9 +300,9 @@ __device__ __forceinline__ void rank_and_stage(SortLds<VALS, ITEMS>& sh, const u
     else
         rank_in_wave<DIG, VALS, BITS, false, ITEMS>(sh.cnt[wave], key, val, dr, seg, n, dig);
     __syncthreads();
-    chunk_bases(sh.cnt, sh.gbase, sh.gdelta, sh.s_wave, &sh.s_real, B);
+    tile_bases(sh.cnt, sh.gbase, sh.gdelta, sh.s_wave, &sh.s_real, B);
     __syncthreads();
-    // Stage the chunk ordered by bucket, equal buckets in input order.
+    // Stage the tile ordered by bucket, equal buckets in input order.
 #pragma unroll
     for (int s = 0; s < ITEMS; ++s) {
         const uint32_t p = sh.cnt[wave][dr[s] >> 16] + (dr[s] & 0xFFFFu);
@@ -311,7 +314,7 @@ __device__ __forceinline__ void rank_and_stage(SortLds<VALS, ITEMS>& sh, const u
     __syncthreads();
 }
 
-// Each bucket's run of the staged chunk goes to its slots; the spare
+// Each bucket's run of the staged tile goes to its slots; the spare
 // bucket's keys, staged last, are not written.
 template <typename DIG, int VALS, int BITS, int ITEMS>
 __device__ __forceinline__ void write_runs(const SortLds<VALS, ITEMS>& sh, uint32_t* __restrict__ keys_out,
@@ -386,19 +389,19 @@ __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
 {
     __shared__ SortLds<VALS, ITEMS> sh;
     const int64_t tile = xcd_contiguous_tile();
-    const int64_t chunk = tile * (int64_t)(kThreads * ITEMS);
-    if (chunk >= n) return;  // uniform over the workgroup
+    const int64_t first = tile * (int64_t)(kThreads * ITEMS);
+    if (first >= n) return;  // uniform over the workgroup
     // The tile's keys are requested first, so their latency overlaps the
     // reads of its column of the scanned table.
     uint32_t key[ITEMS], val[ITEMS];
-    const bool whole = load_chunk<VALS, ITEMS>(keys, vals_in, n, chunk, key, val);
+    const bool whole = load_tile<VALS, ITEMS>(keys, vals_in, n, first, key, val);
     if (moe.hist) {
         moe_bases(sh.gbase, sh.s_wave, slots, tiles, tile, dig.buckets, moe, n);
     } else {
         for (uint32_t d = threadIdx.x; d < dig.buckets; d += kThreads) sh.gbase[d] = slots[(int64_t)d * tiles + tile];
     }
     __syncthreads();
-    rank_and_stage<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, n, dig, chunk);
+    rank_and_stage<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, n, dig, first);
     write_runs<DIG, VALS, BITS, ITEMS>(sh, keys_out, vals_out, dig, out_cap);
 }
 
