@@ -16,7 +16,8 @@ seeded (datagen). Prints one JSON line:
              16 host threads)
   extras     the same-pattern copy, the three-pass scan, cold-cache scans,
              the other workloads' scans (one tile, 1M int32, fp32 10M
-             inclusive, int64 100M), and (unless --no-compact / --no-sort)
+             inclusive, int64 100M), the small ones also replayed from a HIP
+             graph, and (unless --no-compact / --no-sort)
              compaction of 268,435,456
              uint32 keys (ordered and both unordered forms), one 8-bit
              counting-sort pass over those keys (with and without values) and
@@ -367,6 +368,40 @@ def main():
         key = f"{name}_{'incl' if incl else 'excl'}"
         extras[f"{key}_us"] = round(ms * 1e3, 2)
         extras[f"{key}_alg_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    # The same small scans replayed from a HIP graph of 20 launches: the time per
+    # launch is then the kernels', not the host's launch path (each replay's
+    # result is checked against the eager one first).
+    def graph_time(x_np, dcode, incl, calls=20, replays=10):
+        dx = torch.from_numpy(x_np).to(dev)
+        dy, ref = torch.empty_like(dx), torch.empty_like(dx)
+        if L.ds_scan(dcode, incl, 0, dx.data_ptr(), ref.data_ptr(), x_np.size, sh):
+            raise ds.DevscanError(1, "ds_scan")
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):  # allocates the capture stream's workspace outside the capture
+            L.ds_scan(dcode, incl, 0, dx.data_ptr(), dy.data_ptr(), x_np.size, cap.cuda_stream)
+        cap.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(calls):
+                L.ds_scan(dcode, incl, 0, dx.data_ptr(), dy.data_ptr(), x_np.size, cap.cuda_stream)
+        dy.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(dy, ref):
+            log("graph replay differs from the eager scan")
+            sys.exit(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(replays):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / (calls * replays)
+    for name, dcode, incl in (("one_tile", ds.DS_INT32, 0), ("mid", ds.DS_INT32, 0)):
+        extras[f"{name}_{'incl' if incl else 'excl'}_graph_us"] = round(
+            graph_time(datagen.workload(name), dcode, incl) * 1e3, 2)
     x64 = datagen.uniform_i64(64, n, 40)
     for incl in (0, 1):
         ms, nbytes = config_time(x64, ds.DS_INT64, incl)
