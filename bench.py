@@ -457,6 +457,35 @@ def main():
             m_ms = timed(lambda: L.ds_moe_align(ids.data_ptr(), na, e, block, counts.data_ptr(), offsets.data_ptr(),
                                                 srt.data_ptr(), cap, sh), reps=20)
             extras[f"moe_align_{name}_us"] = round(m_ms * 1e3, 1)
+            # replayed from a HIP graph of 20 calls (checked against the eager call first)
+            ref = [t_.clone() for t_ in (counts, offsets, srt)]
+            cap_s = torch.cuda.Stream()
+            cap_s.wait_stream(stream)
+            with torch.cuda.stream(cap_s):  # the capture stream's table and workspace, outside the capture
+                L.ds_moe_align(ids.data_ptr(), na, e, block, counts.data_ptr(), offsets.data_ptr(), srt.data_ptr(),
+                               cap, cap_s.cuda_stream)
+            cap_s.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_s):
+                for _ in range(20):
+                    L.ds_moe_align(ids.data_ptr(), na, e, block, counts.data_ptr(), offsets.data_ptr(),
+                                   srt.data_ptr(), cap, cap_s.cuda_stream)
+            srt.fill_(-9)
+            g.replay()
+            torch.cuda.synchronize()
+            total = int(ref[1][-1].item())
+            if not (torch.equal(counts, ref[0]) and torch.equal(offsets, ref[1])
+                    and torch.equal(srt[:total], ref[2][:total])):
+                log("MoE graph replay differs from the eager call")
+                sys.exit(1)
+            ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ga.record(stream)
+            for _ in range(10):
+                g.replay()
+            gb.record(stream)
+            torch.cuda.synchronize()
+            extras[f"moe_align_{name}_graph_us"] = round(ga.elapsed_time(gb) / 200 * 1e3, 2)
+            del g
 
     cpu = None
     if not args.no_cpu:

@@ -62,3 +62,45 @@ def test_scan_graph_replays(n, inclusive):
     timed_out = ds.query_timeout(stream=cap)
     assert not timed_out, "a look-back wait gave up during the replays"
     del g
+
+
+@pytest.mark.parametrize("name", ["moe_decode", "moe_64k"])
+def test_moe_align_graph_replays(name):
+    # one-launch (256 x 8 ids) and three-launch (65,536 x 8) alignment replayed from a graph
+    t, k, e, block, _, _ = datagen.MOE_WORKLOADS[name]
+    say("graph: MoE alignment", name)
+    ids = datagen.moe_workload(name).ravel()
+    wc, wo, ws = oracle.moe_align(ids, e, block)
+    n = ids.size
+    cap_n = n + e * (block - 1)
+    d_ids = to_dev(ids)
+    counts = torch.empty(e, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(e + 1, dtype=torch.int32, device="cuda")
+    srt = torch.empty(cap_n, dtype=torch.int32, device="cuda")
+
+    def call(stream):
+        return ds.lib.ds_moe_align(d_ids.data_ptr(), n, e, block, counts.data_ptr(), offsets.data_ptr(),
+                                   srt.data_ptr(), cap_n, stream)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        assert call(cap.cuda_stream) == 0  # allocates the table and workspace
+    cap.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for _ in range(CALLS_PER_GRAPH):
+            assert call(cap.cuda_stream) == 0
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        for t_ in (counts, offsets, srt):
+            t_.fill_(-9)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        total = int(wo[-1])
+        assert_int_equal(counts.cpu().numpy(), wc, f"replay {r} counts")
+        assert_int_equal(offsets.cpu().numpy(), wo, f"replay {r} offsets")
+        assert_int_equal(srt.cpu().numpy()[:total], ws, f"replay {r} sorted ids")
+    assert not ds.query_timeout(stream=cap)
+    del g
