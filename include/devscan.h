@@ -110,6 +110,25 @@ int ds_scan(int dtype, int inclusive, int algo, const void* d_in, void* d_out, i
             hipStream_t stream);
 
 /*
+ * One shard of a longer scan: the look-back scan of d_in (`inclusive` 0 or 1)
+ * with every prefix offset by *d_seed, the sum of all elements before this
+ * shard. This is what each GPU would run when a scan is split into
+ * contiguous shards over several GPUs (each reduces its shard, the shard
+ * totals are exchanged and scanned, each scans its shard seeded with its
+ * offset): the multi-block scheme of "Prefix sum and other parallel
+ * patterns" (section "A device-level scan: scan then propagate") one level
+ * up, with the shard offset in the role of a block's starting offset.
+ *   d_seed  NULL (a seed of 0), or one element of `dtype` in device memory,
+ *           aligned to its size and outside d_out (DS_ERR_MISALIGNED,
+ *           DS_ERR_OVERLAP); read by the kernel when it runs, so earlier work
+ *           on the same stream may produce it. Integers wrap as in the scan;
+ *           an fp32 seed is added in fp32.
+ * Other arguments and errors as scan_exclusive.
+ */
+int ds_scan_seeded(int dtype, int inclusive, const void* d_in, void* d_out, int64_t n, const void* d_seed,
+                   hipStream_t stream);
+
+/*
  * Order-preserving stream compaction: writes, in input order, every d_in[i]
  * with (d_in[i] CMP operand) to d_out[0 .. k) and k to *d_num_selected (one
  * int64 in device memory). "Prefix sum and other parallel patterns", section

@@ -9,10 +9,10 @@ binding: argument checks and marshalling, with torch for device memory and
 streams. Importing it fails when the library is missing.
 """
 from ._binding import (ALGO, CMP, DS_FP32, DS_INT32, DS_INT64, DS_UINT32, DS_UINT64, EXPORTS, LIB_PATH,
-                       TILE_VARIANTS, DevscanError, compact_if, compact_unordered, copy, moe_align, radix_pass, dtype_code, lib, load_library, operand_bits,
-                       query_timeout, release_workspace, scan, scan_exclusive, scan_inclusive, set_spin_limit,
-                       tile_pipeline, tile_scan)
+                       TILE_VARIANTS, DevscanError, compact_if, compact_unordered, copy, dtype_code, lib,
+                       load_library, moe_align, operand_bits, query_timeout, radix_pass, release_workspace, scan,
+                       scan_exclusive, scan_inclusive, scan_seeded, set_spin_limit, tile_pipeline, tile_scan)
 
-__all__ = ["scan", "scan_exclusive", "scan_inclusive", "compact_if", "compact_unordered", "radix_pass", "moe_align", "copy", "tile_scan", "tile_pipeline",
-           "query_timeout", "set_spin_limit", "release_workspace", "DevscanError", "lib", "LIB_PATH", "EXPORTS",
-           "ALGO", "CMP", "TILE_VARIANTS"]
+__all__ = ["scan", "scan_exclusive", "scan_inclusive", "scan_seeded", "compact_if", "compact_unordered",
+           "radix_pass", "moe_align", "copy", "tile_scan", "tile_pipeline", "query_timeout", "set_spin_limit",
+           "release_workspace", "DevscanError", "lib", "LIB_PATH", "EXPORTS", "ALGO", "CMP", "TILE_VARIANTS"]

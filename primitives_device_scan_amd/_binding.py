@@ -21,7 +21,7 @@ CMP = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
 ALGO = {"default": 0, "lookback": 1, "three_pass": 2}
 DS_OK = 0
 
-EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "compact_if", "ds_compact_unordered", "ds_radix_pass",
+EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "ds_scan_seeded", "compact_if", "ds_compact_unordered", "ds_radix_pass",
            "ds_moe_align", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
            "ds_tile_elems", "ds_scan_tile_elems", "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace",
            "ds_version"]
@@ -41,6 +41,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(L, name).restype = I
     L.ds_scan.argtypes = [I, I, I, P, P, I64, P]
     L.ds_scan.restype = I
+    L.ds_scan_seeded.argtypes = [I, I, P, P, I64, P, P]
+    L.ds_scan_seeded.restype = I
     L.compact_if.argtypes = [I, P, P, P, I64, I, ctypes.c_uint64, P]
     L.compact_if.restype = I
     L.ds_compact_unordered.argtypes = [I, P, P, P, I64, I, ctypes.c_uint64, I, P]
@@ -125,6 +127,26 @@ def scan(x: torch.Tensor, inclusive: bool, out: torch.Tensor | None = None, *, a
     with torch.cuda.device(x.device):
         _check(lib.ds_scan(code, int(bool(inclusive)), ALGO[algo], x.data_ptr(), out.data_ptr(), x.numel(),
                            _stream_handle(x, stream)), "ds_scan")
+    return out
+
+
+def scan_seeded(x: torch.Tensor, inclusive: bool, seed: torch.Tensor | None, out: torch.Tensor | None = None, *,
+                stream=None) -> torch.Tensor:
+    """One shard of a longer scan: the scan of x with every prefix offset by seed
+    (a one-element GPU tensor of x's dtype, or None for 0)."""
+    _check_tensor(x, "x")
+    code = dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    _check_tensor(out, "out")
+    if out.dtype != x.dtype or out.numel() != x.numel() or out.device != x.device:
+        raise ValueError("out must match x in dtype, size and device")
+    if seed is not None and (seed.dtype != x.dtype or seed.numel() != 1 or seed.device != x.device):
+        raise ValueError("seed must be one element of x's dtype on x's device")
+    with torch.cuda.device(x.device):
+        _check(lib.ds_scan_seeded(code, int(bool(inclusive)), x.data_ptr(), out.data_ptr(), x.numel(),
+                                  None if seed is None else seed.data_ptr(), _stream_handle(x, stream)),
+               "ds_scan_seeded")
     return out
 
 

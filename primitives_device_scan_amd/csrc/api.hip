@@ -165,7 +165,10 @@ int check_io(int dtype, const void* in, const void* out, int64_t n, bool allow_s
     return DS_OK;
 }
 
-int scan_impl(int dtype, int inclusive, int algo, const void* in, void* out, int64_t n, hipStream_t stream)
+// seed (look-back only): null, or one element of dtype in device memory added
+// to every prefix.
+int scan_impl(int dtype, int inclusive, int algo, const void* in, void* out, int64_t n, hipStream_t stream,
+              const void* seed = nullptr)
 {
     if (inclusive != 0 && inclusive != 1) return DS_ERR_INVALID_VALUE;
     if (algo < DS_ALGO_DEFAULT || algo > DS_ALGO_THREE_PASS) return DS_ERR_INVALID_VALUE;
@@ -190,7 +193,7 @@ int scan_impl(int dtype, int inclusive, int algo, const void* in, void* out, int
     if (three) {
         e = ds::launch_three_pass_scan(kind_of(dtype), inclusive != 0, in, out, n, dws, stream);
     } else {
-        e = ds::launch_lookback_scan(kind_of(dtype), inclusive != 0, in, out, n, dws, g_spin_limit, stream);
+        e = ds::launch_lookback_scan(kind_of(dtype), inclusive != 0, in, out, n, dws, g_spin_limit, stream, seed);
         if (w && e == hipSuccess) ++w->lookback_launches;
     }
     return e == hipSuccess ? DS_OK : DS_ERR_HIP;
@@ -213,6 +216,20 @@ int scan_inclusive(int dtype, const void* d_in, void* d_out, int64_t n, hipStrea
 int ds_scan(int dtype, int inclusive, int algo, const void* d_in, void* d_out, int64_t n, hipStream_t stream)
 {
     return scan_impl(dtype, inclusive, algo, d_in, d_out, n, stream);
+}
+
+int ds_scan_seeded(int dtype, int inclusive, const void* d_in, void* d_out, int64_t n, const void* d_seed,
+                   hipStream_t stream)
+{
+    if (inclusive != 0 && inclusive != 1) return DS_ERR_INVALID_VALUE;
+    const int st = check_io(dtype, d_in, d_out, n, true);  // the input and output first, as for every scan
+    if (st != DS_OK || n == 0) return st;
+    if (d_seed) {
+        const int64_t sz = elem_bytes(dtype);
+        if ((uintptr_t)d_seed % sz) return DS_ERR_MISALIGNED;
+        if (overlaps(d_seed, (size_t)sz, d_out, (size_t)(n * sz))) return DS_ERR_OVERLAP;
+    }
+    return scan_impl(dtype, inclusive, DS_ALGO_LOOKBACK, d_in, d_out, n, stream, d_seed);
 }
 
 int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected, int64_t n, int cmp,

@@ -66,16 +66,18 @@ __device__ __forceinline__ uint32_t launch_epoch(Ctrl* ctrl)
 }
 
 // The exclusive prefix of `tile`, found by wave 0 and shared through LDS.
-// Tile 0 publishes its aggregate as its inclusive prefix at once.
+// Tile 0's prefix is `first` (0, or the seed of a seeded scan); it publishes
+// first + aggregate as its inclusive prefix at once.
 template <typename T>
 __device__ __forceinline__ T tile_prefix(int64_t tile, int64_t num_tiles, uint32_t epoch, T agg, Ctrl* ctrl,
-                                         uint64_t* status, uint32_t spin_limit)
+                                         uint64_t* status, uint32_t spin_limit, T first = T(0))
 {
     __shared__ T s_prefix;
     if (threadIdx.x < kWave) {
         T p = T(0);
         if (tile == 0) {
-            if (threadIdx.x == 0) StatusCodec<T>::publish(status, 0, epoch, kFlagPrefix, agg);
+            p = first;
+            if (threadIdx.x == 0) StatusCodec<T>::publish(status, 0, epoch, kFlagPrefix, first + agg);
         } else {
             p = lookback<T>(status, tile, epoch, agg, spin_limit, &ctrl->timeout);
         }

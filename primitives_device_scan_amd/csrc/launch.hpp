@@ -23,8 +23,11 @@ int64_t three_pass_tile_elems(int elem_bytes);  // three-pass scan tile
 int64_t compact_tile_elems(int elem_bytes);     // compaction tile
 int64_t tile_bytes();
 
+// seed: null, or one element of the scan's type in device memory added to
+// every prefix (a seeded scan: one shard of a longer sequence).
 hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
-                                const DevWs& ws, uint32_t spin_limit, hipStream_t stream);
+                                const DevWs& ws, uint32_t spin_limit, hipStream_t stream,
+                                const void* seed = nullptr);
 
 hipError_t launch_three_pass_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
                                   const DevWs& ws, hipStream_t stream);

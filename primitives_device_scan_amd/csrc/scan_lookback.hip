@@ -10,7 +10,8 @@ namespace ds {
 template <typename T, bool INCLUSIVE, bool VEC, int VPT>
 __global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_kernel(const T* in, T* out, int64_t n,
                                                                   int64_t num_tiles, Ctrl* ctrl,
-                                                                  uint64_t* status, uint32_t spin_limit)
+                                                                  uint64_t* status, uint32_t spin_limit,
+                                                                  const T* seed)
 {
     using S = Shape<T, VPT>;
     constexpr int V = S::kPerVec;
@@ -32,8 +33,11 @@ __global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_ker
 
     T wave_excl;
     const T agg = tile_scan_in_wave<T, V, VPT, INCLUSIVE>(e, wave_excl, s_wave);
+    // A seeded scan starts from *seed (the sum of everything before this
+    // input, e.g. earlier shards); only tile 0 reads it, the look-back carries it on.
+    const T first = (seed != nullptr && tile == 0) ? *seed : T(0);
     const T prefix =
-        num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit) : T(0);
+        num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit, first) : first;
     add_uniform(e, prefix + wave_excl);
 
     if (whole)
@@ -63,46 +67,46 @@ static int lookback_vpt(int64_t n)
 
 template <typename T, bool INCL, bool VEC, int VPT>
 static hipError_t lookback_launch(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
-                                  hipStream_t st)
+                                  const void* seed, hipStream_t st)
 {
     const int64_t tiles = (n + Shape<T, VPT>::kTile - 1) / Shape<T, VPT>::kTile;
     if (tiles > 1 && (!ws.ctrl || !ws.status)) return hipErrorInvalidValue;  // several tiles need a workspace
     lookback_scan_kernel<T, INCL, VEC, VPT><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
-        (const T*)in, (T*)out, n, tiles, ws.ctrl, ws.status, spin);
+        (const T*)in, (T*)out, n, tiles, ws.ctrl, ws.status, spin, (const T*)seed);
     return hipGetLastError();
 }
 
 template <typename T, bool INCL, bool VEC>
 static hipError_t lookback_typed(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
-                                 hipStream_t st)
+                                 const void* seed, hipStream_t st)
 {
     switch (lookback_vpt<T, INCL>(n)) {
-    case kSmallScanVPT: return lookback_launch<T, INCL, VEC, kSmallScanVPT>(in, out, n, ws, spin, st);
-    case kMidScanVPT: return lookback_launch<T, INCL, VEC, kMidScanVPT>(in, out, n, ws, spin, st);
-    default: return lookback_launch<T, INCL, VEC, ScanVPT<T, INCL>::value>(in, out, n, ws, spin, st);
+    case kSmallScanVPT: return lookback_launch<T, INCL, VEC, kSmallScanVPT>(in, out, n, ws, spin, seed, st);
+    case kMidScanVPT: return lookback_launch<T, INCL, VEC, kMidScanVPT>(in, out, n, ws, spin, seed, st);
+    default: return lookback_launch<T, INCL, VEC, ScanVPT<T, INCL>::value>(in, out, n, ws, spin, seed, st);
     }
 }
 
 template <typename T>
 static hipError_t lookback_dispatch(bool incl, const void* in, void* out, int64_t n, const DevWs& ws,
-                                    uint32_t spin, hipStream_t st)
+                                    uint32_t spin, const void* seed, hipStream_t st)
 {
     const bool vec = aligned16(in) && aligned16(out);
     if (incl)
-        return vec ? lookback_typed<T, true, true>(in, out, n, ws, spin, st)
-                   : lookback_typed<T, true, false>(in, out, n, ws, spin, st);
-    return vec ? lookback_typed<T, false, true>(in, out, n, ws, spin, st)
-               : lookback_typed<T, false, false>(in, out, n, ws, spin, st);
+        return vec ? lookback_typed<T, true, true>(in, out, n, ws, spin, seed, st)
+                   : lookback_typed<T, true, false>(in, out, n, ws, spin, seed, st);
+    return vec ? lookback_typed<T, false, true>(in, out, n, ws, spin, seed, st)
+               : lookback_typed<T, false, false>(in, out, n, ws, spin, seed, st);
 }
 
 hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
-                                const DevWs& ws, uint32_t spin_limit, hipStream_t stream)
+                                const DevWs& ws, uint32_t spin_limit, hipStream_t stream, const void* seed)
 {
     switch (kind) {
-    case kF32: return lookback_dispatch<float>(inclusive, in, out, n, ws, spin_limit, stream);
+    case kF32: return lookback_dispatch<float>(inclusive, in, out, n, ws, spin_limit, seed, stream);
     case kU64:
-    case kI64: return lookback_dispatch<uint64_t>(inclusive, in, out, n, ws, spin_limit, stream);
-    default: return lookback_dispatch<uint32_t>(inclusive, in, out, n, ws, spin_limit, stream);
+    case kI64: return lookback_dispatch<uint64_t>(inclusive, in, out, n, ws, spin_limit, seed, stream);
+    default: return lookback_dispatch<uint32_t>(inclusive, in, out, n, ws, spin_limit, seed, stream);
     }
 }
 

@@ -80,6 +80,20 @@ def test_ds_scan_validation(lib):
     assert lib.ds_scan(2, 1, 2, A, A + 8, 10, None) == 3
 
 
+def test_scan_seeded_validation(lib):
+    f = lib.ds_scan_seeded
+    S = 0x7F0000200000
+    assert f(7, 0, A, B, 10, S, None) == 2         # DS_ERR_UNSUPPORTED_DTYPE
+    assert f(0, 2, A, B, 10, S, None) == 1         # inclusive not 0/1
+    assert f(0, 0, A, B, -1, S, None) == 1
+    assert f(0, 0, None, None, 0, S, None) == 0    # n == 0: nothing to do
+    assert f(0, 0, A, B, 10, S + 2, None) == 4     # seed misaligned for int32
+    assert f(3, 0, A, B, 10, S + 4, None) == 4     # ... and for int64
+    assert f(0, 0, A, B, 10, B + 8, None) == 3     # seed inside the output
+    assert f(0, 0, A, A + 4, 10, S, None) == 3     # partial overlap of in and out
+    assert f(0, 0, A, B, 1 << 40, S, None) == 7
+
+
 def test_compact_validation(lib):
     C = 0x7F0000200000
     assert lib.compact_if(9, A, B, C, 10, 0, 0, None) == 2
