@@ -6,7 +6,7 @@
 // token dispatch" and exercise 2).
 //
 // Three launches, reduce-then-scan style:
-//   1. digit_count_kernel: each tile (kThreads * ITEMS keys) counts its
+//   1. digit_count_kernel: each tile (kSortThreads * ITEMS keys) counts its
 //      digits in LDS and writes count[d * tiles + tile] -- a digit-major
 //      table;
 //   2. the device-wide exclusive scan of that table (the look-back scan): the
@@ -32,15 +32,21 @@
 
 namespace ds {
 
-// Keys per lane per tile (a tile is kThreads * ITEMS keys). Longer tiles
+// Workgroups of 512 threads (8 waves): for the same tile, each wave ranks
+// half as many slots in sequence as with 256, and the CU holds more waves
+// to cover the latency between the tile's barriers.
+constexpr int kSortThreads = 512;
+constexpr int kSortWaves = kSortThreads / kWave;
+
+// Keys per lane per tile (a tile is kSortThreads * ITEMS keys). Longer tiles
 // give longer runs per digit, so fewer partly written lines, and fewer
 // barriers per key, until registers and LDS cut the workgroups per CU: the
-// keys-only radix pass holds 24 per lane (4 workgroups per CU), with values
-// 20 (the staged values take LDS too; 3 workgroups per CU); MoE inputs are
-// small, and shorter tiles give more workgroups.
-constexpr int kRadixItems = 24;                       // 6,144-key tiles
-constexpr int kRadixKvItems = 20;                     // 5,120-key tiles
-constexpr int kMoeItems = 8;                          // 2,048-id tiles
+// keys-only radix pass holds 16 per lane (3 workgroups per CU), with values
+// 12 (the staged values take LDS too); MoE inputs are small, and shorter
+// tiles give more workgroups.
+constexpr int kRadixItems = 16;                       // 8,192-key tiles
+constexpr int kRadixKvItems = 12;                     // 6,144-key tiles
+constexpr int kMoeItems = 4;                          // 2,048-id tiles
 constexpr int kSortMaxBuckets = 512;                  // real buckets + the spare one
 
 // digit<BITS>(k) is the same bucket as operator(), BITS = ceil(log2(buckets))
@@ -116,21 +122,21 @@ __device__ __forceinline__ int64_t xcd_contiguous_tile()
 }
 
 template <typename DIG, bool VEC>
-__global__ __launch_bounds__(kThreads) void digit_count_kernel(const uint32_t* __restrict__ keys, int64_t n,
+__global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                                  DIG dig, int tile_elems,
                                                                  uint32_t* __restrict__ table, int64_t tiles)
 {
-    __shared__ uint32_t hist[kWaves][kSortMaxBuckets];
+    __shared__ uint32_t hist[kSortWaves][kSortMaxBuckets];
     const uint32_t B = dig.buckets;
     const int wave = (int)(threadIdx.x / kWave);
-    for (uint32_t i = threadIdx.x; i < kWaves * kSortMaxBuckets; i += kThreads) (&hist[0][0])[i] = 0;
+    for (uint32_t i = threadIdx.x; i < kSortWaves * kSortMaxBuckets; i += kSortThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
     const int64_t tile = xcd_contiguous_tile();
     const int64_t base = tile * tile_elems;
     if (VEC && base + tile_elems <= n) {
         const u32x4* p = reinterpret_cast<const u32x4*>(keys + base);
 #pragma unroll 4
-        for (int v = threadIdx.x; v < tile_elems / 4; v += kThreads) {
+        for (int v = threadIdx.x; v < tile_elems / 4; v += kSortThreads) {
             const u32x4 k = __builtin_nontemporal_load(p + v);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -139,22 +145,22 @@ __global__ __launch_bounds__(kThreads) void digit_count_kernel(const uint32_t* _
             }
         }
     } else {
-        for (int i = threadIdx.x; i < tile_elems; i += kThreads) {
+        for (int i = threadIdx.x; i < tile_elems; i += kSortThreads) {
             if (base + i >= n) break;
             const uint32_t d = dig(keys[base + i]);
             if (d < B) atomicAdd(&hist[wave][d], 1u);
         }
     }
     __syncthreads();
-    for (uint32_t d = threadIdx.x; d < B; d += kThreads) {
+    for (uint32_t d = threadIdx.x; d < B; d += kSortThreads) {
         uint32_t c = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) c += hist[w][d];
+        for (int w = 0; w < kSortWaves; ++w) c += hist[w][d];
         table[(int64_t)d * tiles + tile] = c;
     }
 }
 
-// Exclusive scan over the workgroup of one value per thread (256 threads);
+// Exclusive scan over the workgroup of one value per thread;
 // returns this thread's exclusive prefix and sets `total`.
 __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t* s_wave, uint32_t& total)
 {
@@ -164,7 +170,7 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t* s_
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kSortWaves; ++w) {
         const uint32_t t = s_wave[w];
         if (w < wave) before += t;
         all += t;
@@ -173,56 +179,44 @@ __device__ __forceinline__ uint32_t block_exclusive_u32(uint32_t v, uint32_t* s_
     return before + incl - v;
 }
 
-// Buckets d0 = 2t and d1 = 2t + 1 of thread t: the four waves' counts in
-// `cnt` become each wave's first staging position for the bucket; gdelta[d]
-// becomes (output slot of the tile's first bucket-d key) - (its staging
-// position); gbase[d] moves past this tile's bucket-d keys.
+// Bucket d = t of thread t: the waves' counts in `cnt` become each wave's
+// first staging position for the bucket; gdelta[d] becomes (output slot of
+// the tile's first bucket-d key) - (its staging position); gbase[d] moves
+// past this tile's bucket-d keys.
 __device__ __forceinline__ void tile_bases(uint32_t (*cnt)[kSortMaxBuckets], uint32_t* gbase, uint32_t* gdelta,
-                                            uint32_t* s_wave, uint32_t* s_real, uint32_t B)
+                                           uint32_t* s_wave, uint32_t* s_real, uint32_t B)
 {
-    const uint32_t d0 = 2 * threadIdx.x, d1 = d0 + 1;
-    uint32_t p0[kWaves], p1[kWaves], tot0 = 0, tot1 = 0;
+    static_assert(kSortThreads == kSortMaxBuckets, "one bucket per thread");
+    const uint32_t d = threadIdx.x;
+    uint32_t p[kSortWaves], tot = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        p0[w] = tot0;
-        p1[w] = tot1;
-        if (d0 <= B) tot0 += cnt[w][d0];
-        if (d1 <= B) tot1 += cnt[w][d1];
+    for (int w = 0; w < kSortWaves; ++w) {
+        p[w] = tot;
+        if (d <= B) tot += cnt[w][d];
     }
     uint32_t all;
-    const uint32_t start0 = block_exclusive_u32(tot0 + tot1, s_wave, all);
-    const uint32_t start1 = start0 + tot0;
-    if (d0 <= B) {
+    const uint32_t start = block_exclusive_u32(tot, s_wave, all);
+    if (d <= B) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) cnt[w][d0] = start0 + p0[w];
-        if (d0 < B) {
-            gdelta[d0] = gbase[d0] - start0;
-            gbase[d0] += tot0;
+        for (int w = 0; w < kSortWaves; ++w) cnt[w][d] = start + p[w];
+        if (d < B) {
+            gdelta[d] = gbase[d] - start;
+            gbase[d] += tot;
         } else {
-            *s_real = start0;  // keys of real buckets come first in the staging order
-        }
-    }
-    if (d1 <= B) {
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) cnt[w][d1] = start1 + p1[w];
-        if (d1 < B) {
-            gdelta[d1] = gbase[d1] - start1;
-            gbase[d1] += tot1;
-        } else {
-            *s_real = start1;
+            *s_real = start;  // keys of real buckets come first in the staging order
         }
     }
 }
 
-// LDS of a workgroup that ranks and scatters its tile of kThreads * ITEMS keys.
+// LDS of a workgroup that ranks and scatters its tile of kSortThreads * ITEMS keys.
 template <int VALS, int ITEMS>
 struct SortLds {
-    uint32_t cnt[kWaves][kSortMaxBuckets];  // per wave: running count, then staging base
+    uint32_t cnt[kSortWaves][kSortMaxBuckets];  // per wave: running count, then staging base
     uint32_t gbase[kSortMaxBuckets];        // next output slot of each bucket
     uint32_t gdelta[kSortMaxBuckets];       // output slot - staging position
-    uint32_t stage_k[kThreads * ITEMS];
-    uint32_t stage_v[VALS ? kThreads * ITEMS : 1];
-    uint32_t s_wave[kWaves];
+    uint32_t stage_k[kSortThreads * ITEMS];
+    uint32_t stage_v[VALS ? kSortThreads * ITEMS : 1];
+    uint32_t s_wave[kSortWaves];
     uint32_t s_real;
 };
 
@@ -306,7 +300,7 @@ __device__ __forceinline__ void rank_and_stage(SortLds<VALS, ITEMS>& sh, const u
 #pragma unroll
     for (int s = 0; s < ITEMS; ++s) {
         const uint32_t p = sh.cnt[wave][dr[s] >> 16] + (dr[s] & 0xFFFFu);
-        if (p < (uint32_t)(kThreads * ITEMS)) {
+        if (p < (uint32_t)(kSortThreads * ITEMS)) {
             sh.stage_k[p] = key[s];
             if constexpr (VALS != 0) sh.stage_v[p] = val[s];
         }
@@ -322,7 +316,7 @@ __device__ __forceinline__ void write_runs(const SortLds<VALS, ITEMS>& sh, uint3
 {
     const uint32_t B = dig.buckets;
     const uint32_t real = sh.s_real;
-    for (uint32_t j = threadIdx.x; j < real; j += kThreads) {
+    for (uint32_t j = threadIdx.x; j < real; j += kSortThreads) {
         const uint32_t k = sh.stage_k[j];
         const uint32_t d = dig.template digit<BITS>(k);
         const uint64_t pos = (uint64_t)(uint32_t)(sh.gdelta[d] + j);
@@ -345,51 +339,41 @@ struct MoeSlots {
 };
 
 // gbase[e] for MoE: expert e's padded start plus the keys of e in earlier
-// tiles. Thread t takes experts 2t and 2t + 1.
+// tiles. Thread e takes expert e.
 __device__ __forceinline__ void moe_bases(uint32_t* gbase, uint32_t* s_wave, const uint32_t* __restrict__ slots,
                                           int64_t tiles, int64_t tile, uint32_t E, const MoeSlots& moe, int64_t n)
 {
-    const uint32_t e0 = 2 * threadIdx.x, e1 = e0 + 1;
+    const uint32_t e = threadIdx.x;
     const uint32_t last = slots[(int64_t)E * tiles - 1] + moe.hist[(int64_t)E * tiles - 1];
-    uint32_t lo0 = 0, lo1 = 0, c0 = 0, c1 = 0;
-    if (e0 < E) {
-        lo0 = slots[(int64_t)e0 * tiles];
-        c0 = (e0 + 1 < E ? slots[(int64_t)(e0 + 1) * tiles] : last) - lo0;
-    }
-    if (e1 < E) {
-        lo1 = slots[(int64_t)e1 * tiles];
-        c1 = (e1 + 1 < E ? slots[(int64_t)(e1 + 1) * tiles] : last) - lo1;
+    uint32_t lo = 0, c = 0;
+    if (e < E) {
+        lo = slots[(int64_t)e * tiles];
+        c = (e + 1 < E ? slots[(int64_t)(e + 1) * tiles] : last) - lo;
     }
     const uint32_t b = (uint32_t)moe.block;
-    const uint32_t r0 = (c0 + b - 1) / b * b, r1 = (c1 + b - 1) / b * b;
+    const uint32_t r = (c + b - 1) / b * b;
     uint32_t total;
-    const uint32_t off0 = block_exclusive_u32(r0 + r1, s_wave, total), off1 = off0 + r0;
-    if (e0 < E) gbase[e0] = off0 + (slots[(int64_t)e0 * tiles + tile] - lo0);
-    if (e1 < E) gbase[e1] = off1 + (slots[(int64_t)e1 * tiles + tile] - lo1);
+    const uint32_t off = block_exclusive_u32(r, s_wave, total);
+    if (e < E) gbase[e] = off + (slots[(int64_t)e * tiles + tile] - lo);
     if (blockIdx.x == 0) {
-        if (e0 < E) {
-            moe.counts[e0] = (int32_t)c0;
-            moe.offsets[e0] = (int32_t)off0;
-            for (uint32_t j = c0; j < r0; ++j) moe.sorted[off0 + j] = (int32_t)n;
-        }
-        if (e1 < E) {
-            moe.counts[e1] = (int32_t)c1;
-            moe.offsets[e1] = (int32_t)off1;
-            for (uint32_t j = c1; j < r1; ++j) moe.sorted[off1 + j] = (int32_t)n;
+        if (e < E) {
+            moe.counts[e] = (int32_t)c;
+            moe.offsets[e] = (int32_t)off;
+            for (uint32_t j = c; j < r; ++j) moe.sorted[off + j] = (int32_t)n;
         }
         if (threadIdx.x == 0) moe.offsets[E] = (int32_t)total;
     }
 }
 
 template <typename DIG, int VALS, int BITS, int ITEMS>
-__global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
+__global__ __launch_bounds__(kSortThreads) void digit_scatter_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, int64_t n, DIG dig, const uint32_t* __restrict__ slots, MoeSlots moe,
     int64_t tiles, int64_t out_cap)
 {
     __shared__ SortLds<VALS, ITEMS> sh;
     const int64_t tile = xcd_contiguous_tile();
-    const int64_t first = tile * (int64_t)(kThreads * ITEMS);
+    const int64_t first = tile * (int64_t)(kSortThreads * ITEMS);
     if (first >= n) return;  // uniform over the workgroup
     // The tile's keys are requested first, so their latency overlaps the
     // reads of its column of the scanned table.
@@ -398,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void digit_scatter_kernel(
     if (moe.hist) {
         moe_bases(sh.gbase, sh.s_wave, slots, tiles, tile, dig.buckets, moe, n);
     } else {
-        for (uint32_t d = threadIdx.x; d < dig.buckets; d += kThreads) sh.gbase[d] = slots[(int64_t)d * tiles + tile];
+        for (uint32_t d = threadIdx.x; d < dig.buckets; d += kSortThreads) sh.gbase[d] = slots[(int64_t)d * tiles + tile];
     }
     __syncthreads();
     rank_and_stage<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, n, dig, first);
@@ -506,9 +490,9 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
                                       const MoeSlots& moe, int64_t out_cap, const DevWs& ws, uint32_t spin_limit,
                                       hipStream_t st)
 {
-    const int tile_elems = kThreads * ITEMS;
+    const int tile_elems = kSortThreads * ITEMS;
     const int64_t tiles = (n + tile_elems - 1) / tile_elems;
-    const dim3 grid((unsigned)tiles), block(kThreads);
+    const dim3 grid((unsigned)tiles), block(kSortThreads);
     if (aligned16(keys))
         digit_count_kernel<DIG, true><<<grid, block, 0, st>>>(keys, n, dig, tile_elems, hist, tiles);
     else
@@ -541,8 +525,8 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
 
 
 int64_t moe_one_launch_max() { return kMoeOneLaunchMax; }
-int64_t sort_tile_elems(bool values) { return (int64_t)kThreads * (values ? kRadixKvItems : kRadixItems); }
-int64_t moe_tile_elems() { return (int64_t)kThreads * kMoeItems; }
+int64_t sort_tile_elems(bool values) { return (int64_t)kSortThreads * (values ? kRadixKvItems : kRadixItems); }
+int64_t moe_tile_elems() { return (int64_t)kSortThreads * kMoeItems; }
 int sort_max_buckets() { return kSortMaxBuckets - 1; }
 
 hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out, uint32_t* vals_out,
