@@ -281,8 +281,9 @@ int64_t ds_tile_elems(int dtype, int entry);
  * Elements per workgroup tile of the look-back scan (scan_exclusive,
  * scan_inclusive, ds_scan look-back) for an input of n elements of `dtype`:
  * 8 sixteen-byte vectors per thread up to 8 MiB of data, 12 up to 32 MiB,
- * the type's large tile beyond (so mid-size inputs still spread over many
- * workgroups). `inclusive` 0 or 1. Returns -1 for invalid arguments.
+ * 16 up to 64 MiB (where that is below the type's large tile), the type's
+ * large tile beyond (so mid-size inputs still spread over many workgroups).
+ * `inclusive` 0 or 1. Returns -1 for invalid arguments.
  */
 int64_t ds_scan_tile_elems(int dtype, int inclusive, int64_t n);
 

@@ -47,14 +47,16 @@ __global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_ker
 }
 
 // Vectors per thread for n elements: the per-type large tile (ScanVPT) from
-// 32 MiB of data on, where resident bytes must hide the look-back; below, a
+// 64 MiB of data on, where resident bytes must hide the look-back; below, a
 // large tile would leave most CUs idle (1M int32 fill 41 workgroups of 96 KiB)
-// and a small last tile costs element-wise loads, so mid-size inputs take 12
-// vectors per thread and inputs up to 8 MiB take 8 (measured: one 4,096-int32
-// tile 7.9 -> 3.8 us, 1M int32 10.0 -> 5.6 us, 8M int32 14.5 -> 13.5 us per
-// launch back to back; from 30M on the large tile is fastest).
+// and a small last tile costs element-wise loads, so inputs up to 8 MiB take
+// 8 vectors per thread, up to 32 MiB 12 and up to 64 MiB 16 (measured: one
+// 4,096-int32 tile 7.9 -> 3.8 us, 1M int32 10.0 -> 5.6 us, 8M int32 14.5 ->
+// 13.5 us, 12M fp32 inclusive 19.6 -> 17.7 us per launch back to back; from
+// 30M int32 on the large tile is fastest).
 constexpr int kSmallScanVPT = 8;
 constexpr int kMidScanVPT = 12;
+constexpr int kUpperScanVPT = 16;
 
 template <typename T, bool INCL>
 static int lookback_vpt(int64_t n)
@@ -62,6 +64,7 @@ static int lookback_vpt(int64_t n)
     const int64_t bytes = n * (int64_t)sizeof(T);
     if (bytes <= ((int64_t)8 << 20)) return kSmallScanVPT;
     if (bytes <= ((int64_t)32 << 20)) return kMidScanVPT;
+    if (bytes <= ((int64_t)64 << 20) && kUpperScanVPT < ScanVPT<T, INCL>::value) return kUpperScanVPT;
     return ScanVPT<T, INCL>::value;
 }
 
@@ -83,6 +86,7 @@ static hipError_t lookback_typed(const void* in, void* out, int64_t n, const Dev
     switch (lookback_vpt<T, INCL>(n)) {
     case kSmallScanVPT: return lookback_launch<T, INCL, VEC, kSmallScanVPT>(in, out, n, ws, spin, seed, st);
     case kMidScanVPT: return lookback_launch<T, INCL, VEC, kMidScanVPT>(in, out, n, ws, spin, seed, st);
+    case kUpperScanVPT: return lookback_launch<T, INCL, VEC, kUpperScanVPT>(in, out, n, ws, spin, seed, st);
     default: return lookback_launch<T, INCL, VEC, ScanVPT<T, INCL>::value>(in, out, n, ws, spin, seed, st);
     }
 }

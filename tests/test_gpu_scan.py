@@ -128,14 +128,17 @@ def test_edge_sizes(dt, algo):
 
 def _regime_sizes(dt, inc):
     """Sizes at the tile boundaries of each look-back tile regime (8 vectors per thread up to
-    8 MiB of data, 12 up to 32 MiB, the large tile beyond) and at the regime boundaries."""
+    8 MiB of data, 12 up to 32 MiB, 16 up to 64 MiB, the large tile beyond) and at the regime
+    boundaries."""
     esz = np.dtype(dt).itemsize
-    small_max, mid_max = (8 << 20) // esz, (32 << 20) // esz
-    ts, tm, tl = scan_tile(dt, inc, 1), scan_tile(dt, inc, small_max + 1), scan_tile(dt, inc, mid_max + 1)
-    assert ts < tm < tl or (ts < tm and tl >= tm), (ts, tm, tl)
-    km, kl = small_max // tm + 2, mid_max // tl + 1
+    small_max, mid_max, upper_max = (8 << 20) // esz, (32 << 20) // esz, (64 << 20) // esz
+    ts, tm = scan_tile(dt, inc, 1), scan_tile(dt, inc, small_max + 1)
+    tu, tl = scan_tile(dt, inc, mid_max + 1), scan_tile(dt, inc, upper_max + 1)
+    assert ts < tm < tu <= tl, (ts, tm, tu, tl)
+    km, ku, kl = small_max // tm + 2, mid_max // tu + 1, upper_max // tl + 1
     return [ts - 1, ts, ts + 1, 7 * ts + 3, small_max, small_max + 1, km * tm - 1, km * tm, km * tm + 1,
-            mid_max, mid_max + 1, kl * tl - 1, kl * tl, kl * tl + 1]
+            mid_max, mid_max + 1, ku * tu - 1, ku * tu, ku * tu + 1,
+            upper_max, upper_max + 1, kl * tl - 1, kl * tl, kl * tl + 1]
 
 
 @pytest.mark.parametrize("dt", [np.int32, np.float32, np.int64], ids=lambda d: np.dtype(d).name)
