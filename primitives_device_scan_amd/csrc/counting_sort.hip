@@ -121,34 +121,49 @@ __device__ __forceinline__ int64_t xcd_contiguous_tile()
     return (int64_t)(x * q + (x < r ? x : r) + b / 8u);
 }
 
-template <typename DIG, bool VEC>
+// All of a lane's keys are loaded before any is counted: the LDS atomics
+// would otherwise keep the compiler from issuing the next load until the
+// previous one has returned, one 16-byte load in flight per lane.
+template <typename DIG, bool VEC, int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_t* __restrict__ keys, int64_t n,
-                                                                 DIG dig, int tile_elems,
-                                                                 uint32_t* __restrict__ table, int64_t tiles)
+                                                                 DIG dig, uint32_t* __restrict__ table,
+                                                                 int64_t tiles)
 {
+    static_assert(ITEMS % 4 == 0, "whole 16-byte vectors per lane");
+    constexpr int kTile = kSortThreads * ITEMS, kVecs = ITEMS / 4;
     __shared__ uint32_t hist[kSortWaves][kSortMaxBuckets];
     const uint32_t B = dig.buckets;
     const int wave = (int)(threadIdx.x / kWave);
     for (uint32_t i = threadIdx.x; i < kSortWaves * kSortMaxBuckets; i += kSortThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
     const int64_t tile = xcd_contiguous_tile();
-    const int64_t base = tile * tile_elems;
-    if (VEC && base + tile_elems <= n) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(keys + base);
-#pragma unroll 4
-        for (int v = threadIdx.x; v < tile_elems / 4; v += kSortThreads) {
-            const u32x4 k = __builtin_nontemporal_load(p + v);
+    const int64_t base = tile * kTile;
+    if (VEC && base + kTile <= n) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(keys + base) + threadIdx.x;
+        u32x4 k[kVecs];
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v) k[v] = __builtin_nontemporal_load(p + v * kSortThreads);
+        __syncthreads();  // the histograms are zero
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t d = dig(k[j]);
-                if (d < B) atomicAdd(&hist[wave][d], 1u);
+                const uint32_t d = dig(k[v][j]);
+                if (!DIG::kSpareKeys || d < B) atomicAdd(&hist[wave][d], 1u);
             }
-        }
     } else {
-        for (int i = threadIdx.x; i < tile_elems; i += kSortThreads) {
-            if (base + i >= n) break;
-            const uint32_t d = dig(keys[base + i]);
-            if (d < B) atomicAdd(&hist[wave][d], 1u);
+        // the ragged last tile, or keys not 16-byte aligned: element by element, guarded
+        uint32_t k[ITEMS];
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int64_t at = base + threadIdx.x + (int64_t)i * kSortThreads;
+            k[i] = at < n ? keys[at] : 0u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int64_t at = base + threadIdx.x + (int64_t)i * kSortThreads;
+            const uint32_t d = dig(k[i]);
+            if (at < n && d < B) atomicAdd(&hist[wave][d], 1u);
         }
     }
     __syncthreads();
@@ -494,9 +509,9 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
     const int64_t tiles = (n + tile_elems - 1) / tile_elems;
     const dim3 grid((unsigned)tiles), block(kSortThreads);
     if (aligned16(keys))
-        digit_count_kernel<DIG, true><<<grid, block, 0, st>>>(keys, n, dig, tile_elems, hist, tiles);
+        digit_count_kernel<DIG, true, ITEMS><<<grid, block, 0, st>>>(keys, n, dig, hist, tiles);
     else
-        digit_count_kernel<DIG, false><<<grid, block, 0, st>>>(keys, n, dig, tile_elems, hist, tiles);
+        digit_count_kernel<DIG, false, ITEMS><<<grid, block, 0, st>>>(keys, n, dig, hist, tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_lookback_scan(kU32, false, hist, slots, (int64_t)dig.buckets * tiles, ws, spin_limit, st);
