@@ -22,8 +22,9 @@
  * in an order the library chooses; they meet |y_i - exact_i| <= 1e-5 *
  * sum_{j<=i} |x_j| at the sizes the tests cover, and may differ in the last
  * bits from run to run (the look-back can stop at different tiles).
- * Pointers must be aligned to the element size; 16-byte aligned buffers take
- * the vectorised path, other aligned buffers a slower scalar one.
+ * Pointers must be aligned to the element size. Any such pointer takes the
+ * 16-byte vector path (a slice that starts mid-vector, x + 1 say, costs a few
+ * percent); only the ragged end of the data goes element by element.
  */
 #ifndef DEVSCAN_H
 #define DEVSCAN_H

@@ -38,7 +38,8 @@ __device__ __forceinline__ void wave_lds_sync()
 
 constexpr int kGroup = 8;  // vector indices per staging round: 8 KiB of LDS per wave
 
-template <typename T, bool VEC, int CMP>
+// IN_A16: `in` is 16-byte aligned (whole waves load 16-byte vectors either way).
+template <typename T, bool IN_A16, int CMP>
 __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* out, int64_t* num_selected,
                                                                int64_t n, int64_t num_tiles, T operand, Ctrl* ctrl,
                                                                uint64_t* status, uint32_t spin_limit)
@@ -56,10 +57,10 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
     const uint32_t epoch = (num_tiles > 1 && wave == 0) ? launch_epoch(ctrl) : 0u;
 
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
-    const bool whole = VEC && seg + S::kWaveElems <= n;
+    const bool whole = seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T, kCompactVPT>(in, seg, lane, e);
+        load_vec<T, kCompactVPT, IN_A16>(in, seg, lane, e);
     else
         load_scalar<T, kCompactVPT>(in, seg, n, lane, e, T(0));
 
@@ -88,13 +89,16 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
     const bool fits = (int64_t)prefix + agg <= n;
     if (!fits && threadIdx.x == 0) flag_timeout(ctrl);
     const int64_t wave_base = (int64_t)prefix + wave_excl;  // output index of this wave's first kept element
+    // Elements of `out` before its first 16-byte boundary's phase: the runs are
+    // staged so that every full vector written lands 16-byte aligned.
+    const uint32_t out_phase = (uint32_t)(((uintptr_t)out % kVecBytes) / sizeof(T));
     T* const stage = s_stage[wave];
 #pragma unroll
     for (int g = 0; g < kCompactVPT; g += kGroup) {
         const uint32_t start = readlane(off[g], 0);  // rank of the round's first kept element in the wave
         const uint32_t end = g + kGroup < kCompactVPT ? readlane(off[g + kGroup], 0) : wave_total;
         const int64_t first = wave_base + start;
-        const uint32_t shift = VEC ? (uint32_t)(first % V) : 0u;
+        const uint32_t shift = (uint32_t)((first + out_phase) % V);
 #pragma unroll
         for (int k = g; k < g + kGroup; ++k) {
             uint32_t r = off[k] - start + shift;
@@ -104,20 +108,16 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
         }
         wave_lds_sync();
         const uint32_t span = shift + (end - start);  // staged slots, the shift included
-        T* const dst = out + (first - shift);         // 16-byte aligned when VEC
+        T* const dst = out + (first - shift);         // 16-byte aligned; nothing below out is written
         if (fits) {
-            if (VEC) {
-                for (uint32_t q = (uint32_t)lane * V; q < span; q += kWave * V) {
-                    if (q >= shift && q + V <= span) {
-                        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + q),
-                                                    reinterpret_cast<u32x4*>(dst + q));
-                    } else {
-                        for (uint32_t i = q; i < q + V && i < span; ++i)
-                            if (i >= shift) dst[i] = stage[i];
-                    }
+            for (uint32_t q = (uint32_t)lane * V; q < span; q += kWave * V) {
+                if (q >= shift && q + V <= span) {
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + q),
+                                                reinterpret_cast<u32x4*>(dst + q));
+                } else {
+                    for (uint32_t i = q; i < q + V && i < span; ++i)
+                        if (i >= shift) dst[i] = stage[i];
                 }
-            } else {
-                for (uint32_t i = lane; i < span; i += kWave) dst[i] = stage[i];
             }
         }
         wave_lds_sync();
@@ -131,7 +131,7 @@ static hipError_t compact_cmp(const void* in, void* out, int64_t* num_selected, 
 {
     const int64_t tiles = (n + Shape<T, kCompactVPT>::kTile - 1) / Shape<T, kCompactVPT>::kTile;
     if (tiles > 1 && (!ws.ctrl || !ws.status)) return hipErrorInvalidValue;  // several tiles need a workspace
-    if (aligned16(in) && aligned16(out))
+    if (aligned16(in))
         compact_kernel<T, true, CMP><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
             (const T*)in, (T*)out, num_selected, n, tiles, operand, ws.ctrl, ws.status, spin);
     else

@@ -33,7 +33,7 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
 
 __global__ void zero_count_kernel(uint64_t* count) { *count = 0; }
 
-template <typename T, bool VEC, int CMP, bool PER_WG>
+template <typename T, bool IN_A16, int CMP, bool PER_WG>
 __global__ __launch_bounds__(kThreads) void compact_unordered_kernel(const T* in, T* out, uint64_t* count,
                                                                       int64_t n, T operand)
 {
@@ -44,10 +44,10 @@ __global__ __launch_bounds__(kThreads) void compact_unordered_kernel(const T* in
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
     const int64_t seg = (int64_t)blockIdx.x * S::kTile + (int64_t)wave * S::kWaveElems;
-    const bool whole = VEC && seg + S::kWaveElems <= n;
+    const bool whole = seg + S::kWaveElems <= n;  // 16-byte vectors, `in` 16-byte aligned or not (IN_A16)
     T e[S::kItems];
     if (whole)
-        load_vec<T, kCompactVPT>(in, seg, lane, e);
+        load_vec<T, kCompactVPT, IN_A16>(in, seg, lane, e);
     else
         load_scalar<T, kCompactVPT>(in, seg, n, lane, e, T(0));
 
@@ -97,13 +97,13 @@ static hipError_t unordered_cmp(const void* in, void* out, int64_t* count, int64
 {
     const unsigned tiles = (unsigned)((n + Shape<T, kCompactVPT>::kTile - 1) / Shape<T, kCompactVPT>::kTile);
     const dim3 grid(tiles), block(kThreads);
-    const bool vec = aligned16(in);
+    const bool a16 = aligned16(in);
     zero_count_kernel<<<dim3(1), dim3(1), 0, st>>>((uint64_t*)count);
     if (per_wg) {
-        if (vec) compact_unordered_kernel<T, true, CMP, true><<<grid, block, 0, st>>>((const T*)in, (T*)out, (uint64_t*)count, n, operand);
+        if (a16) compact_unordered_kernel<T, true, CMP, true><<<grid, block, 0, st>>>((const T*)in, (T*)out, (uint64_t*)count, n, operand);
         else compact_unordered_kernel<T, false, CMP, true><<<grid, block, 0, st>>>((const T*)in, (T*)out, (uint64_t*)count, n, operand);
     } else {
-        if (vec) compact_unordered_kernel<T, true, CMP, false><<<grid, block, 0, st>>>((const T*)in, (T*)out, (uint64_t*)count, n, operand);
+        if (a16) compact_unordered_kernel<T, true, CMP, false><<<grid, block, 0, st>>>((const T*)in, (T*)out, (uint64_t*)count, n, operand);
         else compact_unordered_kernel<T, false, CMP, false><<<grid, block, 0, st>>>((const T*)in, (T*)out, (uint64_t*)count, n, operand);
     }
     return hipGetLastError();

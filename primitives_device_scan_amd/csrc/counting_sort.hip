@@ -124,7 +124,8 @@ __device__ __forceinline__ int64_t xcd_contiguous_tile()
 // All of a lane's keys are loaded before any is counted: the LDS atomics
 // would otherwise keep the compiler from issuing the next load until the
 // previous one has returned, one 16-byte load in flight per lane.
-template <typename DIG, bool VEC, int ITEMS>
+// A16: keys 16-byte aligned (whole tiles load 16-byte vectors either way).
+template <typename DIG, bool A16, int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                                  DIG dig, uint32_t* __restrict__ table,
                                                                  int64_t tiles)
@@ -137,9 +138,10 @@ __global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_
     for (uint32_t i = threadIdx.x; i < kSortWaves * kSortMaxBuckets; i += kSortThreads) (&hist[0][0])[i] = 0;
     const int64_t tile = xcd_contiguous_tile();
     const int64_t base = tile * kTile;
-    if (VEC && base + kTile <= n) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(keys + base) + threadIdx.x;
-        u32x4 k[kVecs];
+    if (base + kTile <= n) {
+        using V = typename VecOf<A16>::type;
+        const V* p = reinterpret_cast<const V*>(keys + base) + threadIdx.x;
+        V k[kVecs];
 #pragma unroll
         for (int v = 0; v < kVecs; ++v) k[v] = __builtin_nontemporal_load(p + v * kSortThreads);
         __syncthreads();  // the histograms are zero
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_
                 if (!DIG::kSpareKeys || d < B) atomicAdd(&hist[wave][d], 1u);
             }
     } else {
-        // the ragged last tile, or keys not 16-byte aligned: element by element, guarded
+        // the ragged last tile: element by element, guarded
         uint32_t k[ITEMS];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {

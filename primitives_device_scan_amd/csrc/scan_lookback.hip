@@ -7,7 +7,7 @@
 
 namespace ds {
 
-template <typename T, bool INCLUSIVE, bool VEC, int VPT>
+template <typename T, bool INCLUSIVE, bool A16, int VPT>
 __global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_kernel(const T* in, T* out, int64_t n,
                                                                   int64_t num_tiles, Ctrl* ctrl,
                                                                   uint64_t* status, uint32_t spin_limit,
@@ -24,10 +24,12 @@ __global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_ker
     const uint32_t epoch = (num_tiles > 1 && wave == 0) ? launch_epoch(ctrl) : 0u;
 
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
-    const bool whole = VEC && seg + S::kWaveElems <= n;
+    // Whole waves take 16-byte vectors whatever the alignment (A16: in and out
+    // are 16-byte aligned); the ragged end goes element by element.
+    const bool whole = seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T, VPT>(in, seg, lane, e);
+        load_vec<T, VPT, A16>(in, seg, lane, e);
     else
         load_scalar<T, VPT>(in, seg, n, lane, e, T(0));
 
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_ker
     add_uniform(e, prefix + wave_excl);
 
     if (whole)
-        store_vec<T, VPT>(out, seg, lane, e);
+        store_vec<T, VPT, A16>(out, seg, lane, e);
     else
         store_scalar<T, VPT>(out, seg, n, lane, e);
 }
@@ -68,26 +70,26 @@ static int lookback_vpt(int64_t n)
     return ScanVPT<T, INCL>::value;
 }
 
-template <typename T, bool INCL, bool VEC, int VPT>
+template <typename T, bool INCL, bool A16, int VPT>
 static hipError_t lookback_launch(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
                                   const void* seed, hipStream_t st)
 {
     const int64_t tiles = (n + Shape<T, VPT>::kTile - 1) / Shape<T, VPT>::kTile;
     if (tiles > 1 && (!ws.ctrl || !ws.status)) return hipErrorInvalidValue;  // several tiles need a workspace
-    lookback_scan_kernel<T, INCL, VEC, VPT><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+    lookback_scan_kernel<T, INCL, A16, VPT><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
         (const T*)in, (T*)out, n, tiles, ws.ctrl, ws.status, spin, (const T*)seed);
     return hipGetLastError();
 }
 
-template <typename T, bool INCL, bool VEC>
+template <typename T, bool INCL, bool A16>
 static hipError_t lookback_typed(const void* in, void* out, int64_t n, const DevWs& ws, uint32_t spin,
                                  const void* seed, hipStream_t st)
 {
     switch (lookback_vpt<T, INCL>(n)) {
-    case kSmallScanVPT: return lookback_launch<T, INCL, VEC, kSmallScanVPT>(in, out, n, ws, spin, seed, st);
-    case kMidScanVPT: return lookback_launch<T, INCL, VEC, kMidScanVPT>(in, out, n, ws, spin, seed, st);
-    case kUpperScanVPT: return lookback_launch<T, INCL, VEC, kUpperScanVPT>(in, out, n, ws, spin, seed, st);
-    default: return lookback_launch<T, INCL, VEC, ScanVPT<T, INCL>::value>(in, out, n, ws, spin, seed, st);
+    case kSmallScanVPT: return lookback_launch<T, INCL, A16, kSmallScanVPT>(in, out, n, ws, spin, seed, st);
+    case kMidScanVPT: return lookback_launch<T, INCL, A16, kMidScanVPT>(in, out, n, ws, spin, seed, st);
+    case kUpperScanVPT: return lookback_launch<T, INCL, A16, kUpperScanVPT>(in, out, n, ws, spin, seed, st);
+    default: return lookback_launch<T, INCL, A16, ScanVPT<T, INCL>::value>(in, out, n, ws, spin, seed, st);
     }
 }
 
@@ -95,11 +97,11 @@ template <typename T>
 static hipError_t lookback_dispatch(bool incl, const void* in, void* out, int64_t n, const DevWs& ws,
                                     uint32_t spin, const void* seed, hipStream_t st)
 {
-    const bool vec = aligned16(in) && aligned16(out);
+    const bool a16 = aligned16(in) && aligned16(out);
     if (incl)
-        return vec ? lookback_typed<T, true, true>(in, out, n, ws, spin, seed, st)
+        return a16 ? lookback_typed<T, true, true>(in, out, n, ws, spin, seed, st)
                    : lookback_typed<T, true, false>(in, out, n, ws, spin, seed, st);
-    return vec ? lookback_typed<T, false, true>(in, out, n, ws, spin, seed, st)
+    return a16 ? lookback_typed<T, false, true>(in, out, n, ws, spin, seed, st)
                : lookback_typed<T, false, false>(in, out, n, ws, spin, seed, st);
 }
 

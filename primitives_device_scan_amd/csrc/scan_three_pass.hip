@@ -7,7 +7,7 @@
 
 namespace ds {
 
-template <typename T, bool VEC>
+template <typename T, bool A16>
 __global__ __launch_bounds__(kThreads) void tile_reduce_kernel(const T* in, int64_t n, T* totals)
 {
     using S = Shape<T, kThreePassVPT>;
@@ -17,8 +17,8 @@ __global__ __launch_bounds__(kThreads) void tile_reduce_kernel(const T* in, int6
     const int64_t tile = blockIdx.x;
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
     T e[S::kItems];
-    if (VEC && seg + S::kWaveElems <= n)
-        load_vec<T, kThreePassVPT>(in, seg, lane, e);
+    if (seg + S::kWaveElems <= n)  // whole wave: 16-byte vectors, 16-byte aligned or not (A16)
+        load_vec<T, kThreePassVPT, A16>(in, seg, lane, e);
     else
         load_scalar<T, kThreePassVPT>(in, seg, n, lane, e, T(0));
     T s = T(0);
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kTotalsThreads) void scan_totals_kernel(T* totals, 
     }
 }
 
-template <typename T, bool INCLUSIVE, bool VEC>
+template <typename T, bool INCLUSIVE, bool A16>
 __global__ __launch_bounds__(kThreads) void tile_rescan_kernel(const T* in, T* out, int64_t n,
                                                                 const T* offsets)
 {
@@ -77,10 +77,10 @@ __global__ __launch_bounds__(kThreads) void tile_rescan_kernel(const T* in, T* o
     const int wave = (int)(threadIdx.x / kWave);
     const int64_t tile = blockIdx.x;
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
-    const bool whole = VEC && seg + S::kWaveElems <= n;
+    const bool whole = seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T, kThreePassVPT>(in, seg, lane, e);
+        load_vec<T, kThreePassVPT, A16>(in, seg, lane, e);
     else
         load_scalar<T, kThreePassVPT>(in, seg, n, lane, e, T(0));
     T off[kThreePassVPT];
@@ -88,29 +88,29 @@ __global__ __launch_bounds__(kThreads) void tile_rescan_kernel(const T* in, T* o
     tile_local_scan<T, V, kThreePassVPT>(e, off, wave_excl, s_wave);
     tile_finish<T, V, kThreePassVPT, INCLUSIVE>(e, off, wave_excl, offsets[tile]);
     if (whole)
-        store_vec<T, kThreePassVPT>(out, seg, lane, e);
+        store_vec<T, kThreePassVPT, A16>(out, seg, lane, e);
     else
         store_scalar<T, kThreePassVPT>(out, seg, n, lane, e);
 }
 
-template <typename T, bool VEC>
+template <typename T, bool A16>
 static hipError_t three_pass_typed(bool incl, const void* in, void* out, int64_t n, const DevWs& ws,
                                    hipStream_t st)
 {
     const int64_t tiles = (n + Shape<T, kThreePassVPT>::kTile - 1) / Shape<T, kThreePassVPT>::kTile;
     if (!ws.totals) return hipErrorInvalidValue;
     T* totals = (T*)ws.totals;
-    tile_reduce_kernel<T, VEC><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>((const T*)in, n, totals);
+    tile_reduce_kernel<T, A16><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>((const T*)in, n, totals);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     scan_totals_kernel<T><<<dim3(1), dim3(kTotalsThreads), 0, st>>>(totals, tiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (incl)
-        tile_rescan_kernel<T, true, VEC><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+        tile_rescan_kernel<T, true, A16><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
             (const T*)in, (T*)out, n, totals);
     else
-        tile_rescan_kernel<T, false, VEC><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
+        tile_rescan_kernel<T, false, A16><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
             (const T*)in, (T*)out, n, totals);
     return hipGetLastError();
 }

@@ -23,6 +23,13 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kVecBytes = 16;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte access
+// The same 16 bytes at an address that is only 4-byte aligned (a tensor slice
+// that starts mid-vector). Global 16-byte accesses need dword alignment only,
+// so these still compile to one dwordx4 load or store per lane; a wave's
+// 1 KiB then straddles one more 128-byte line.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+template <bool A16> struct VecOf { using type = u32x4; };
+template <> struct VecOf<false> { using type = u32x4_a4; };
 
 // VPT = 16-byte vectors per thread; the tile is kThreads * VPT * 16 bytes.
 template <typename T, int VPT>
@@ -110,15 +117,17 @@ __device__ __forceinline__ int64_t elem_index(int64_t seg, int k, int j, int lan
     return seg + (int64_t)(k * kWave + lane) * (kVecBytes / (int)sizeof(T)) + j;
 }
 
-// Whole wave segment in range and 16-byte aligned: one 16-byte load per vector.
-template <typename T, int VPT>
+// Whole wave segment in range: one 16-byte load per vector. A16: `in` is
+// 16-byte aligned (else only element-aligned).
+template <typename T, int VPT, bool A16 = true>
 __device__ __forceinline__ void load_vec(const T* __restrict__ in, int64_t seg, int lane,
                                          T (&e)[Shape<T, VPT>::kItems])
 {
-    const u32x4* p = reinterpret_cast<const u32x4*>(in + seg) + lane;
+    using V = typename VecOf<A16>::type;
+    const V* p = reinterpret_cast<const V*>(in + seg) + lane;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const u32x4 r = __builtin_nontemporal_load(p + k * kWave);
+        const V r = __builtin_nontemporal_load(p + k * kWave);
         __builtin_memcpy(&e[k * Shape<T, VPT>::kPerVec], &r, kVecBytes);
     }
 }
@@ -138,14 +147,15 @@ __device__ __forceinline__ void load_scalar(const T* __restrict__ in, int64_t se
         }
 }
 
-template <typename T, int VPT>
+template <typename T, int VPT, bool A16 = true>
 __device__ __forceinline__ void store_vec(T* __restrict__ out, int64_t seg, int lane,
                                           const T (&e)[Shape<T, VPT>::kItems])
 {
-    u32x4* p = reinterpret_cast<u32x4*>(out + seg) + lane;
+    using V = typename VecOf<A16>::type;
+    V* p = reinterpret_cast<V*>(out + seg) + lane;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        u32x4 r;
+        V r;
         __builtin_memcpy(&r, &e[k * Shape<T, VPT>::kPerVec], kVecBytes);
         __builtin_nontemporal_store(r, p + k * kWave);
     }

@@ -2,6 +2,7 @@
 the kept elements in order, bit-exact."""
 import numpy as np
 import pytest
+import torch
 
 import datagen
 import oracle
@@ -71,7 +72,7 @@ def test_compact_all_and_none():
 
 @pytest.mark.parametrize("dt", [np.uint32, np.float32, np.int64])
 def test_compact_misaligned(dt):
-    # one element off 16-byte alignment: the element-wise load path
+    # input and output one element off 16-byte alignment
     T = tile_of(dt, compact=True)
     case = [c for c in pins.COMPACT_CASES if c[0] == dt][0]
     for n in (T - 1, 5 * T + 3):
@@ -81,3 +82,38 @@ def test_compact_misaligned(dt):
         want = oracle.compact(x, ">", c)
         assert k == want.size
         assert_int_equal(out[:k].view(want.dtype), want, f"{np.dtype(dt).name} n={n} misaligned")
+
+
+@pytest.mark.parametrize("dt", [np.uint32, np.int64])
+def test_compact_misaligned_phases(dt):
+    # input and output at different offsets from 16-byte alignment; the output
+    # buffer keeps its sentinel below the output and past the kept elements
+    import primitives_device_scan_amd as ds
+    from gpu_util import CODE, STORAGE, sentinel_fill, stream_handle, to_dev
+    T = tile_of(dt, compact=True)
+    case = [c for c in pins.COMPACT_CASES if c[0] == dt][0]
+    n = 6 * T + 7
+    x = case[1](4321, n).astype(dt)
+    c = case[2][1]
+    want = oracle.compact(x, ">", c)
+    esz = np.dtype(dt).itemsize
+    per_vec = 16 // esz
+    bits = ds.operand_bits(torch.int64, c)
+    if dt == np.uint32:
+        bits &= 0xFFFFFFFF
+    for in_off, out_off in [(a, b) for a in range(per_vec) for b in range(per_vec) if a != b]:
+        xin = to_dev(x, extra=in_off + 5, offset=in_off)
+        out = torch.empty(n + out_off + 5, dtype=STORAGE[np.dtype(dt)][1], device="cuda")
+        sentinel_fill(out)
+        cnt = torch.full((1,), -7, dtype=torch.int64, device="cuda")
+        st = ds.lib.compact_if(CODE[np.dtype(dt)], xin.data_ptr() + in_off * esz, out.data_ptr() + out_off * esz,
+                               cnt.data_ptr(), n, ds.CMP[">"], bits, stream_handle())
+        assert st == 0, ds.lib.ds_status_string(st)
+        torch.cuda.synchronize()
+        k = int(cnt.item())
+        assert k == want.size, (in_off, out_off)
+        raw = out.view(torch.uint8).cpu().numpy()
+        got = raw[out_off * esz:(out_off + k) * esz].view(want.dtype)
+        assert_int_equal(got, want, f"in +{in_off} out +{out_off}")
+        assert np.all(raw[:out_off * esz] == 0xA5), "written below the output"
+        assert np.all(raw[(out_off + k) * esz:] == 0xA5), "written past the kept elements"

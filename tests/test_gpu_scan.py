@@ -183,6 +183,62 @@ def test_misaligned(dt):
                 check_scan(x, True, gpu_scan(x, True, algo, offset=off), f"offset {off} n={n} {algo}")
 
 
+def _scan_at(x, inclusive, algo, in_off, out_off, guard=37):
+    """Scan with the input `in_off` and the output `out_off` elements past a
+    16-byte boundary; the output buffer's elements around the result keep
+    their sentinel."""
+    import primitives_device_scan_amd as ds
+    from gpu_util import CODE, STORAGE, from_dev, sentinel_fill, stream_handle, to_dev
+    n, esz = x.size, x.dtype.itemsize
+    xin = to_dev(x, extra=in_off + guard, offset=in_off)
+    out = torch.empty(n + out_off + guard, dtype=STORAGE[x.dtype][1], device="cuda")
+    sentinel_fill(out)
+    st = ds.lib.ds_scan(CODE[x.dtype], int(inclusive), ds.ALGO[algo], xin.data_ptr() + in_off * esz,
+                        out.data_ptr() + out_off * esz, n, stream_handle())
+    assert st == 0, ds.lib.ds_status_string(st)
+    torch.cuda.synchronize()
+    raw = out.view(torch.uint8).cpu().numpy()
+    assert np.all(raw[:out_off * esz] == 0xA5), "written below the output"
+    assert np.all(raw[(out_off + n) * esz:] == 0xA5), "written past the output"
+    return from_dev(out, x.dtype, out_off, n)
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda d: np.dtype(d).name)
+def test_misaligned_phases(dt):
+    # input and output at different offsets from 16-byte alignment (one of them
+    # aligned, or both off by different amounts): whole waves use 16-byte
+    # vectors at 4- or 8-byte alignment; several tiles and a ragged end
+    T = tile_of(dt)
+    per_vec = 16 // np.dtype(dt).itemsize
+    n = 7 * T + 5
+    x = _input(dt, n, 123)
+    phases = [(a, b) for a in range(per_vec) for b in range(per_vec) if a != b]
+    for in_off, out_off in phases:
+        for algo in ALGOS:
+            for inc in (False, True):
+                check_scan(x, inc, _scan_at(x, inc, algo, in_off, out_off), f"in +{in_off} out +{out_off} {algo} inc={inc}")
+
+
+@pytest.mark.parametrize("dt", [np.int32, np.float32, np.int64], ids=lambda d: np.dtype(d).name)
+def test_misaligned_largest_tiles(dt):
+    # past 64 MiB the look-back takes its largest tile; one element off alignment on both sides,
+    # then the input alone off alignment
+    n = (80 << 20) // np.dtype(dt).itemsize + 3
+    x = _input(dt, n, 321)
+    say(f"misaligned largest tile {np.dtype(dt).name} n={n}")
+    for inc in (False, True):
+        check_scan(x, inc, _scan_at(x, inc, "lookback", 1, 1), f"both +1 inc={inc}")
+    check_scan(x, False, _scan_at(x, False, "lookback", 1, 0), "input +1, output aligned")
+
+
+def test_misaligned_in_place():
+    n = 9 * tile_of(np.int32) + 11
+    x = datagen.uniform_int(5, n, -1000, 1000)
+    for off in (1, 2, 3):
+        for inc in (False, True):
+            check_scan(x, inc, gpu_scan(x, inc, in_place=True, offset=off), f"in place +{off} inc={inc}")
+
+
 def test_int_repeat_determinism():
     x = datagen.uniform_int(99, 5_000_011, -1000, 1000)
     first = gpu_scan(x, False)
