@@ -354,6 +354,9 @@ def main():
     # inclusive at the headline size, reusing its buffers
     ii_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 1, 0, d_xi.data_ptr(), d_yi.data_ptr(), n, sh))
     extras["int32_incl_100m_us"] = round(ii_ms * 1e3, 1)
+    # both pointers one element past a 16-byte boundary (a tensor slice x[1:])
+    mi_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 0, 0, d_xi.data_ptr() + 4, d_yi.data_ptr() + 4, n - 1, sh))
+    extras["int32_excl_100m_misaligned_us"] = round(mi_ms * 1e3, 1)
     del d_xf, d_yf
 
     # the other workloads' configurations, each as its own launch (median of 20)

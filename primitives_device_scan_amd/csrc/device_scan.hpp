@@ -9,28 +9,29 @@
 namespace ds {
 
 // 16-byte vectors per thread (VPT); a tile is 256 threads x VPT x 16 B.
-//  - look-back scan: the largest tile that fits its occupancy (ScanOcc
-//    below) without spilling (ScanVPT), since resident tile bytes per CU are
-//    what hide the look-back latency (several microseconds under full HBM
-//    load) behind other tiles' transfers: 96 KiB for int32 and fp32
-//    exclusive, 80 KiB inclusive, 80 / 64 KiB for 8-byte types;
+//  - look-back scan: large tiles, since resident tile bytes per CU are what
+//    hide the look-back latency (several microseconds under full HBM load)
+//    behind other tiles' transfers: 112 KiB for 4-byte types (fp32 inclusive
+//    96 KiB), 80 / 64 KiB for 8-byte types, all at 3 workgroups per CU
+//    (ScanOcc). Measured at n = 100M against 96 KiB tiles at 4 per CU for
+//    4-byte types: 1.5-2.5% faster in all four 4-byte cases, though the int32
+//    tiles spill 12 bytes per thread (as the 96 KiB int32 tile did 24 at 4 per
+//    CU); 120-128 KiB tiles, or 2 per CU, were slower, as were larger 8-byte
+//    tiles (they spill 70-430 bytes);
 //  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
 //    wait to hide; compaction's keep mask holds 64 elements).
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
     static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 16 : 20)
-                               : __is_same(T, float) ? (INCLUSIVE ? 20 : 24)
-                                                     : (INCLUSIVE ? 20 : 24);
+                               : __is_same(T, float) ? (INCLUSIVE ? 24 : 28)
+                                                     : 28;
 };
-// Workgroups per CU the look-back kernel is compiled for (waves per SIMD):
-// 4 for 4-byte integers (their tiles fit 128 VGPRs); fp32 and 8-byte scans
-// need more registers per vector and hold larger tiles at 3 (measured: 1-2%
-// faster for fp32, 5-6% for 8-byte than their 4-wave tiles).
+// Workgroups per CU the look-back kernel is compiled for (waves per SIMD).
 template <typename T>
 struct ScanOcc {
-    static constexpr int value = (sizeof(T) == 8 || __is_same(T, float)) ? 3 : 4;
+    static constexpr int value = 3;
 };
-constexpr int kVPT = 24;  // largest scan tile: the same-pattern copy uses it
+constexpr int kVPT = 28;  // largest scan tile: the same-pattern copy uses it
 constexpr int kThreePassVPT = 16;
 constexpr int kCompactVPT = 16;
 constexpr int kTileBytes = kThreads * kVPT * kVecBytes;

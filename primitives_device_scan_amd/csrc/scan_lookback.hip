@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_ker
 
 // Vectors per thread for n elements: the per-type large tile (ScanVPT) from
 // 64 MiB of data on, where resident bytes must hide the look-back; below, a
-// large tile would leave most CUs idle (1M int32 fill 41 workgroups of 96 KiB)
+// large tile would leave most CUs idle (1M int32 fill 35 workgroups of 112 KiB)
 // and a small last tile costs element-wise loads, so inputs up to 8 MiB take
 // 8 vectors per thread, up to 32 MiB 12 and up to 64 MiB 16 (measured: one
 // 4,096-int32 tile 7.9 -> 3.8 us, 1M int32 10.0 -> 5.6 us, 8M int32 14.5 ->
