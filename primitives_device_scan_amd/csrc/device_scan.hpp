@@ -12,24 +12,27 @@ namespace ds {
 //  - look-back scan: large tiles, since resident tile bytes per CU are what
 //    hide the look-back latency (several microseconds under full HBM load)
 //    behind other tiles' transfers: 112 KiB for 4-byte types (fp32 inclusive
-//    96 KiB), 80 / 64 KiB for 8-byte types, all at 3 workgroups per CU
-//    (ScanOcc). Measured at n = 100M against 96 KiB tiles at 4 per CU for
-//    4-byte types: 1.5-2.5% faster in all four 4-byte cases, though the int32
-//    tiles spill 12 bytes per thread (as the 96 KiB int32 tile did 24 at 4 per
-//    CU); 120-128 KiB tiles, or 2 per CU, were slower, as were larger 8-byte
-//    tiles (they spill 70-430 bytes);
+//    96 KiB) at 3 workgroups per CU, 128 / 112 KiB for 8-byte types
+//    (exclusive / inclusive) at 2 per CU (ScanOcc). Measured at n = 100M:
+//    against 96 KiB tiles at 4 per CU, the 4-byte scans 1.5-2.5% faster in all
+//    four cases, though the int32 tiles spill 12 bytes per thread (as the 96
+//    KiB int32 tile did 24 at 4 per CU), while 120-128 KiB tiles or 2 per CU
+//    were slower; against 80 / 64 KiB at 3 per CU, int64 5% (exclusive) and
+//    7% (inclusive) faster; 8-byte tiles of 96-112 KiB at 3 per CU spill
+//    70-430 bytes and are slower, and 160 KiB at 2 per CU too;
 //  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
 //    wait to hide; compaction's keep mask holds 64 elements).
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
-    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 16 : 20)
+    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 32)
                                : __is_same(T, float) ? (INCLUSIVE ? 24 : 28)
                                                      : 28;
 };
-// Workgroups per CU the look-back kernel is compiled for (waves per SIMD).
-template <typename T>
+// Workgroups per CU the look-back kernel is compiled for (waves per SIMD):
+// the large 8-byte tiles need up to 256 VGPRs; every other tile fits 3.
+template <typename T, int VPT>
 struct ScanOcc {
-    static constexpr int value = 3;
+    static constexpr int value = (sizeof(T) == 8 && VPT > 20) ? 2 : 3;
 };
 constexpr int kVPT = 28;  // largest scan tile: the same-pattern copy uses it
 constexpr int kThreePassVPT = 16;

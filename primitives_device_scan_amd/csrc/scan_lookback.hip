@@ -8,7 +8,7 @@
 namespace ds {
 
 template <typename T, bool INCLUSIVE, bool A16, int VPT>
-__global__ __launch_bounds__(kThreads, ScanOcc<T>::value) void lookback_scan_kernel(const T* in, T* out, int64_t n,
+__global__ __launch_bounds__(kThreads, (ScanOcc<T, VPT>::value)) void lookback_scan_kernel(const T* in, T* out, int64_t n,
                                                                   int64_t num_tiles, Ctrl* ctrl,
                                                                   uint64_t* status, uint32_t spin_limit,
                                                                   const T* seed)
