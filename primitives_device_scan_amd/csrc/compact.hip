@@ -40,14 +40,14 @@ constexpr int kGroup = 8;  // vector indices per staging round: 8 KiB of LDS per
 
 // IN_A16: `in` is 16-byte aligned (whole waves load 16-byte vectors either way).
 template <typename T, bool IN_A16, int CMP>
-__global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* out, int64_t* num_selected,
+__global__ __launch_bounds__(kThreads, kCompactOcc) void compact_kernel(const T* in, T* out, int64_t* num_selected,
                                                                int64_t n, int64_t num_tiles, T operand, Ctrl* ctrl,
                                                                uint64_t* status, uint32_t spin_limit)
 {
     using S = Shape<T, kCompactVPT>;
     constexpr int V = S::kPerVec;
     constexpr int kBuf = kWave * V * kGroup + V;  // a round's slices plus the alignment shift
-    static_assert(S::kItems <= 64, "keep mask is 64 bits");
+    constexpr int kMaskWords = (S::kItems + 63) / 64;  // a vector's V bits never straddle two words
     static_assert(kCompactVPT % kGroup == 0, "whole rounds");
     __shared__ uint32_t s_wave[kWaves];
     __shared__ __attribute__((aligned(16))) T s_stage[kWaves][kBuf];
@@ -64,18 +64,19 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
     else
         load_scalar<T, kCompactVPT>(in, seg, n, lane, e, T(0));
 
-    uint64_t keepm = 0;
+    uint64_t keepm[kMaskWords] = {};  // bit i % 64 of word i / 64: this lane keeps element slot i
 #pragma unroll
     for (int k = 0; k < kCompactVPT; ++k)
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             const int i = k * V + j;
-            if ((whole || elem_index<T>(seg, k, j, lane) < n) && keep<CMP>(e[i], operand)) keepm |= 1ull << i;
+            if ((whole || elem_index<T>(seg, k, j, lane) < n) && keep<CMP>(e[i], operand))
+                keepm[i / 64] |= 1ull << (i % 64);
         }
     uint32_t cnt[kCompactVPT];
 #pragma unroll
     for (int k = 0; k < kCompactVPT; ++k)
-        cnt[k] = (uint32_t)__builtin_popcountll((keepm >> (k * V)) & ((1ull << V) - 1));
+        cnt[k] = (uint32_t)__builtin_popcountll((keepm[k * V / 64] >> (k * V % 64)) & ((1ull << V) - 1));
     uint32_t off[kCompactVPT];
     uint32_t wave_excl;
     const uint32_t agg = tile_local_scan<uint32_t, 1, kCompactVPT>(cnt, off, wave_excl, s_wave);
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 4) void compact_kernel(const T* in, T* ou
             uint32_t r = off[k] - start + shift;
 #pragma unroll
             for (int j = 0; j < V; ++j)
-                if ((keepm >> (k * V + j)) & 1ull) stage[r++] = e[k * V + j];
+                if ((keepm[(k * V + j) / 64] >> ((k * V + j) % 64)) & 1ull) stage[r++] = e[k * V + j];
         }
         wave_lds_sync();
         const uint32_t span = shift + (end - start);  // staged slots, the shift included

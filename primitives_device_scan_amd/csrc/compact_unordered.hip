@@ -51,8 +51,7 @@ __global__ __launch_bounds__(kThreads) void compact_unordered_kernel(const T* in
     else
         load_scalar<T, kCompactVPT>(in, seg, n, lane, e, T(0));
 
-    static_assert(S::kItems <= 64, "keep mask is 64 bits");
-    uint64_t keepm = 0;  // bit i: this lane keeps element slot i
+    uint64_t keepm[(S::kItems + 63) / 64] = {};  // bit i % 64 of word i / 64: this lane keeps element slot i
     uint32_t total = 0;
 #pragma unroll
     for (int k = 0; k < kCompactVPT; ++k)
@@ -60,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void compact_unordered_kernel(const T* in
         for (int j = 0; j < V; ++j) {
             const int i = k * V + j;
             const bool kp = (whole || elem_index<T>(seg, k, j, lane) < n) && keep_u<CMP>(e[i], operand);
-            keepm |= (uint64_t)kp << i;
+            keepm[i / 64] |= (uint64_t)kp << (i % 64);
             total += (uint32_t)__builtin_popcountll(ballot(kp));
         }
 
@@ -84,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void compact_unordered_kernel(const T* in
     }
 #pragma unroll
     for (int i = 0; i < S::kItems; ++i) {
-        const bool kp = (keepm >> i) & 1ull;
+        const bool kp = (keepm[i / 64] >> (i % 64)) & 1ull;
         const uint64_t m = ballot(kp);  // the lanes keeping slot i
         if (kp) out[start + lanes_below(m)] = e[i];
         start += (uint64_t)__builtin_popcountll(m);

@@ -37,6 +37,7 @@ struct ScanOcc {
 constexpr int kVPT = 28;  // largest scan tile: the same-pattern copy uses it
 constexpr int kThreePassVPT = 16;
 constexpr int kCompactVPT = 16;
+constexpr int kCompactOcc = 4;  // workgroups per CU the ordered compaction is compiled for
 constexpr int kTileBytes = kThreads * kVPT * kVecBytes;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
