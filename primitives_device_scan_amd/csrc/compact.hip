@@ -109,15 +109,17 @@ __global__ __launch_bounds__(kThreads, kCompactOcc) void compact_kernel(const T*
         }
         wave_lds_sync();
         const uint32_t span = shift + (end - start);  // staged slots, the shift included
-        T* const dst = out + (first - shift);         // 16-byte aligned; nothing below out is written
+        // Output index of staged slot 0: out + dst0 is 16-byte aligned; dst0 may be
+        // below 0, and only slots from `shift` on (indices from `first`) are written.
+        const int64_t dst0 = first - (int64_t)shift;
         if (fits) {
             for (uint32_t q = (uint32_t)lane * V; q < span; q += kWave * V) {
                 if (q >= shift && q + V <= span) {
                     __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + q),
-                                                reinterpret_cast<u32x4*>(dst + q));
+                                                reinterpret_cast<u32x4*>(out + (dst0 + q)));
                 } else {
                     for (uint32_t i = q; i < q + V && i < span; ++i)
-                        if (i >= shift) dst[i] = stage[i];
+                        if (i >= shift) out[dst0 + i] = stage[i];
                 }
             }
         }
