@@ -12,6 +12,13 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* in, u32x4* 
     const int64_t base = (int64_t)blockIdx.x * (kThreads * VPT) +
                          (int64_t)(threadIdx.x / kWave) * (kWave * VPT) + lane_id();
     u32x4 r[VPT];
+    if (base + (VPT - 1) * kWave < nvec) {  // whole wave segment: straight-line, as the scan's
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) r[k] = __builtin_nontemporal_load(in + base + k * kWave);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) __builtin_nontemporal_store(r[k], out + base + k * kWave);
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
         if (base + k * kWave < nvec) r[k] = __builtin_nontemporal_load(in + base + k * kWave);
