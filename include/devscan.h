@@ -260,8 +260,8 @@ int ds_set_spin_limit(uint32_t polls);
 
 /* Which entry point's tile ds_tile_elems reports. */
 typedef enum {
-    DS_TILE_OF_SCAN_EXCLUSIVE = 0, /* scan_exclusive, ds_scan look-back exclusive: the tile of
-                                      inputs over 32 MiB (ds_scan_tile_elems for any n) */
+    DS_TILE_OF_SCAN_EXCLUSIVE = 0, /* scan_exclusive, ds_scan look-back exclusive: the large tile,
+                                      used past 64 MiB of input (ds_scan_tile_elems for any n) */
     DS_TILE_OF_SCAN_INCLUSIVE = 1, /* scan_inclusive, ds_scan look-back inclusive: same */
     DS_TILE_OF_THREE_PASS = 2,     /* DS_ALGO_THREE_PASS */
     DS_TILE_OF_COMPACT = 3,        /* compact_if */
