@@ -70,21 +70,36 @@ __device__ __forceinline__ uint32_t launch_epoch(Ctrl* ctrl)
     return __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Called by one thread as soon as the tile aggregate is known: tile 0
+// publishes its inclusive prefix `first + agg` (first: 0, or the seed of a
+// seeded scan), every other tile its aggregate, so successors can use it
+// while this tile still scans its own elements.
+template <typename T>
+__device__ __forceinline__ void publish_early(uint64_t* status, int64_t tile, uint32_t epoch, T agg, T first)
+{
+    if (tile == 0)
+        StatusCodec<T>::publish(status, 0, epoch, kFlagPrefix, first + agg);
+    else
+        StatusCodec<T>::publish(status, tile, epoch, kFlagAggregate, agg);
+}
+
 // The exclusive prefix of `tile`, found by wave 0 and shared through LDS.
-// Tile 0's prefix is `first` (0, or the seed of a seeded scan); it publishes
-// first + aggregate as its inclusive prefix at once.
+// Tile 0's prefix is `first` (0, or the seed of a seeded scan); unless
+// `published` (publish_early has run), it publishes first + aggregate as its
+// inclusive prefix at once.
 template <typename T>
 __device__ __forceinline__ T tile_prefix(int64_t tile, int64_t num_tiles, uint32_t epoch, T agg, Ctrl* ctrl,
-                                         uint64_t* status, uint32_t spin_limit, T first = T(0))
+                                         uint64_t* status, uint32_t spin_limit, T first = T(0),
+                                         bool published = false)
 {
     __shared__ T s_prefix;
     if (threadIdx.x < kWave) {
         T p = T(0);
         if (tile == 0) {
             p = first;
-            if (threadIdx.x == 0) StatusCodec<T>::publish(status, 0, epoch, kFlagPrefix, first + agg);
+            if (threadIdx.x == 0 && !published) StatusCodec<T>::publish(status, 0, epoch, kFlagPrefix, first + agg);
         } else {
-            p = lookback<T>(status, tile, epoch, agg, spin_limit, &ctrl->timeout);
+            p = lookback<T>(status, tile, epoch, agg, spin_limit, &ctrl->timeout, published);
         }
         if (threadIdx.x == 0) {
             s_prefix = p;

@@ -221,17 +221,40 @@ __device__ __forceinline__ T tile_local_scan(T (&e)[V * VPT], T (&off)[VPT], T& 
     return agg;
 }
 
-// tile_local_scan and fold_wave_offsets in one pass over the vectors: each
-// vector's wave scan is folded into its elements as soon as it is known, so
-// only the data and a few temporaries are live (the separate form keeps every
-// vector's scan and offset live at once). Out: e = each element's inclusive
-// or exclusive sum within its wave's segment, wave_excl = sum of the waves
-// before this one; returns the tile aggregate. One workgroup barrier.
-template <typename T, int V, int VPT, bool INCLUSIVE>
-__device__ __forceinline__ T tile_scan_in_wave(T (&e)[V * VPT], T& wave_excl, T* s_wave)
+// The tile aggregate by a reduction (each lane's elements, then the wave, then
+// the four wave totals through LDS): known before any prefix is computed, so
+// the look-back scan can publish it at once. Out: wave_excl = sum of the
+// waves before this one. One workgroup barrier.
+template <typename T, int N>
+__device__ __forceinline__ T tile_reduce(const T (&e)[N], T& wave_excl, T* s_wave)
 {
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
+    T s = T(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) s = s + e[i];
+    s = wave_sum(s);
+    if (lane == 0) s_wave[wave] = s;
+    __syncthreads();
+    T agg = T(0), before = T(0);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const T v = s_wave[w];
+        if (w < wave) before = before + v;
+        agg = agg + v;
+    }
+    wave_excl = before;
+    return agg;
+}
+
+// tile_local_scan and fold_wave_offsets in one pass over the vectors, within
+// the wave only: each vector's wave scan is folded into its elements as soon
+// as it is known, so only the data and a few temporaries are live (the
+// separate form keeps every vector's scan and offset live at once). Out: e =
+// each element's inclusive or exclusive sum within its wave's segment.
+template <typename T, int V, int VPT, bool INCLUSIVE>
+__device__ __forceinline__ void scan_in_wave(T (&e)[V * VPT])
+{
     T run = T(0);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -252,17 +275,6 @@ __device__ __forceinline__ T tile_scan_in_wave(T (&e)[V * VPT], T& wave_excl, T*
             e[k * V] = off;
         }
     }
-    if (lane == 0) s_wave[wave] = run;
-    __syncthreads();
-    T agg = T(0), before = T(0);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const T v = s_wave[w];
-        if (w < wave) before = before + v;
-        agg = agg + v;
-    }
-    wave_excl = before;
-    return agg;
 }
 
 // Folds the per-vector offsets into the values: e becomes each element's
@@ -375,7 +387,7 @@ struct StatusCodec {
 
 // Decoupled look-back, run by one whole wave for tile `tile` (> 0) once the
 // tile's aggregate is known.
-//  1. Publish the aggregate.
+//  1. Publish the aggregate (unless `published`: the caller already has).
 //  2. Wait, polling with lane 0 alone, until the nearest predecessor has
 //     published anything: until then no window can complete, and polling one
 //     word instead of 64 keeps the status traffic off the memory system.
@@ -389,11 +401,11 @@ struct StatusCodec {
 // missing values count as 0 and `timeout` is set, so every wave finishes.
 template <typename T>
 __device__ T lookback(uint64_t* status, int64_t tile, uint32_t epoch, T agg, uint32_t spin_limit,
-                      uint32_t* timeout)
+                      uint32_t* timeout, bool published = false)
 {
     using C = StatusCodec<T>;
     const int lane = lane_id();
-    if (lane == 0) C::publish(status, tile, epoch, kFlagAggregate, agg);
+    if (lane == 0 && !published) C::publish(status, tile, epoch, kFlagAggregate, agg);
     uint32_t polls = 0;
     bool gave_up = false;
     auto give_up = [&]() {
