@@ -1,8 +1,9 @@
-// scan_lookback.hip -- the single-pass device-wide scan: each tile scans
-// itself in registers, publishes its aggregate, looks back over the status of
-// earlier tiles for its exclusive prefix, publishes its inclusive prefix and
-// writes ("Prefix sum and other parallel patterns", section "A device-level
-// scan: scan then propagate", decoupled look-back).
+// scan_lookback.hip -- the single-pass device-wide scan: each tile sums
+// itself and publishes its aggregate, scans itself in registers while that
+// status travels, looks back over the status of earlier tiles for its
+// exclusive prefix, publishes its inclusive prefix and writes ("Prefix sum and
+// other parallel patterns", section "A device-level scan: scan then
+// propagate", decoupled look-back).
 #include "device_scan.hpp"
 
 namespace ds {
