@@ -12,19 +12,20 @@ namespace ds {
 //  - look-back scan: large tiles, since resident tile bytes per CU are what
 //    hide the look-back latency (several microseconds under full HBM load)
 //    behind other tiles' transfers: 112 KiB for 4-byte types (fp32 inclusive
-//    96 KiB) at 3 workgroups per CU, 128 / 112 KiB for 8-byte types
+//    96 KiB) at 3 workgroups per CU, 144 / 112 KiB for 8-byte types
 //    (exclusive / inclusive) at 2 per CU (ScanOcc). Measured at n = 100M:
 //    against 96 KiB tiles at 4 per CU, the 4-byte scans 1.5-2.5% faster in all
 //    four cases, though the int32 tiles spill 12 bytes per thread (as the 96
 //    KiB int32 tile did 24 at 4 per CU), while 120-128 KiB tiles or 2 per CU
-//    were slower; against 80 / 64 KiB at 3 per CU, int64 5% (exclusive) and
-//    7% (inclusive) faster; 8-byte tiles of 96-112 KiB at 3 per CU spill
-//    70-430 bytes and are slower, and 160 KiB at 2 per CU too;
+//    were slower; against 80 / 64 KiB at 3 per CU, int64 5-6% (exclusive) and
+//    7% (inclusive) faster (144 KiB exclusive tiles 1-1.4% faster than 128);
+//    8-byte tiles of 96-112 KiB at 3 per CU spill 70-430 bytes and are
+//    slower, and 160 KiB at 2 per CU too;
 //  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
 //    wait to hide; compaction's keep mask holds 64 elements).
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
-    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 32)
+    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 36)
                                : __is_same(T, float) ? (INCLUSIVE ? 24 : 28)
                                                      : 28;
 };
