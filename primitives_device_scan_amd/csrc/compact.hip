@@ -22,8 +22,8 @@ __device__ __forceinline__ bool keep(T v, T c)
     return v != c;
 }
 
-// Compaction over the scan's 64 KiB tiles. The keep flags live as one bit per
-// element in a 64-bit mask; the per-vector keep counts go through the same
+// Compaction over 64 KiB tiles. The keep flags live as one bit per element in
+// 64-bit mask words; the per-vector keep counts go through the same
 // wave/tile scan and look-back as a scan of 32-bit counts. Once the tile's
 // output offset is known, each wave moves its kept elements out in rounds of
 // kGroup vector indices: the kept elements of those slices are packed into a
