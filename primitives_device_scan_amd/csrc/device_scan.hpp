@@ -12,7 +12,7 @@ namespace ds {
 //  - look-back scan: large tiles, since resident tile bytes per CU are what
 //    hide the look-back latency (several microseconds under full HBM load)
 //    behind other tiles' transfers: 112 KiB for 4-byte types (fp32 inclusive
-//    96 KiB) at 3 workgroups per CU, 144 / 112 KiB for 8-byte types
+//    104 KiB, the largest that does not spill) at 3 workgroups per CU, 144 / 112 KiB for 8-byte types
 //    (exclusive / inclusive) at 2 per CU (ScanOcc). Measured at n = 100M:
 //    against 96 KiB tiles at 4 per CU, the 4-byte scans 1.5-2.5% faster in all
 //    four cases, though the int32 tiles spill 12 bytes per thread (as the 96
@@ -26,7 +26,7 @@ namespace ds {
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
     static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 36)
-                               : __is_same(T, float) ? (INCLUSIVE ? 24 : 28)
+                               : __is_same(T, float) ? (INCLUSIVE ? 26 : 28)
                                                      : 28;
 };
 // Workgroups per CU the look-back kernel is compiled for (waves per SIMD):
