@@ -16,15 +16,31 @@
  * inside a kernel surfaces, as usual in HIP, at the caller's next
  * synchronisation of the stream.
  *
+ * Bounded waits. The single-pass kernels wait for earlier tiles' status
+ * words; every wait gives up after a spin limit (ds_set_spin_limit), so a
+ * kernel always finishes. A call in which any wait gave up has produced
+ * invalid outputs (compact_if writes -1 as its count when its last tile saw
+ * the give-up); ds_query_timeout reports it and restores the workspace.
+ *
+ * Graph capture. A call records only kernel launches once the workspace of
+ * its (device, stream) is large enough, so make one call of at least the
+ * captured size on the stream before capturing it; otherwise the call
+ * returns DS_ERR_STREAM_CAPTURING and records nothing. Status words carry a
+ * 30-bit launch number that the kernels advance themselves, and the host
+ * clears them every 2^29 eager launches; a captured graph therefore may be
+ * replayed at most 2^29 times before ds_release_workspace() (or one eager
+ * call after 2^29 launches) clears them again.
+ *
  * Element types: DS_INT32 / DS_UINT32 / DS_FP32 (4 bytes) and DS_INT64 /
  * DS_UINT64 (8 bytes), stored contiguously. Integer sums wrap modulo 2^32 or
  * 2^64 (signed and unsigned give the same bits). fp32 sums are fp32 additions
  * in an order the library chooses; they meet |y_i - exact_i| <= 1e-5 *
  * sum_{j<=i} |x_j| at the sizes the tests cover, and may differ in the last
  * bits from run to run (the look-back can stop at different tiles).
- * Pointers must be aligned to the element size. Any such pointer takes the
- * 16-byte vector path (a slice that starts mid-vector, x + 1 say, costs a few
- * percent); only the ragged end of the data goes element by element.
+ * Pointers must be aligned to the element size (DS_ERR_MISALIGNED
+ * otherwise). Any such pointer takes the 16-byte vector path (a slice that
+ * starts mid-vector, x + 1 say, costs a few percent); only the ragged end of
+ * the data goes element by element.
  */
 #ifndef DEVSCAN_H
 #define DEVSCAN_H
@@ -67,10 +83,12 @@ typedef enum {
     DS_ERR_INVALID_VALUE = 1,     /* n < 0, null pointer with n > 0, bad enum value */
     DS_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not one of ds_dtype */
     DS_ERR_OVERLAP = 3,           /* input and output overlap without being the same buffer */
-    DS_ERR_MISALIGNED = 4,        /* a pointer not aligned to the element size */
-    DS_ERR_OUT_OF_MEMORY = 5,     /* workspace allocation failed */
-    DS_ERR_HIP = 6,               /* a HIP runtime call or kernel launch failed */
-    DS_ERR_TOO_LARGE = 7          /* n beyond what the entry point supports */
+    DS_ERR_OUT_OF_MEMORY = 4,     /* workspace allocation failed */
+    DS_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed */
+    DS_ERR_MISALIGNED = 6,        /* a pointer not aligned to the element size */
+    DS_ERR_TOO_LARGE = 7,         /* n beyond what the entry point supports */
+    DS_ERR_STREAM_CAPTURING = 8   /* the workspace would have to be allocated, grown or cleared while
+                                     `stream` is being captured into a graph */
 } ds_status;
 
 /*
@@ -132,7 +150,7 @@ int ds_scan_seeded(int dtype, int inclusive, const void* d_in, void* d_out, int6
 /*
  * Order-preserving stream compaction: writes, in input order, every d_in[i]
  * with (d_in[i] CMP operand) to d_out[0 .. k) and k to *d_num_selected (one
- * int64 in device memory). "Prefix sum and other parallel patterns", section
+ * int64 in device memory; -1 if the last tile saw a look-back wait give up). "Prefix sum and other parallel patterns", section
  * "Stream compaction" and its first exercise: the write position of a kept
  * element is the exclusive scan of the keep flags, k = pos[n-1] + flag[n-1].
  * Flags, positions and the scan of them stay on chip (one launch).
@@ -247,9 +265,20 @@ int ds_tile_pipeline(int dtype, int variant, const void* d_in, void* d_out, int6
  * Waits for `stream` and reports, in *timed_out, whether any look-back wait
  * on this (device, stream) gave up since the last query (1) or not (0), then
  * clears the record. A wait gives up only after the spin limit; the outputs of
- * such a call are not valid. Returns DS_OK or DS_ERR_HIP.
+ * such a call are not valid. After a give-up it also clears every status word
+ * of the workspace (a tile that read the launch number late may have stamped
+ * its word with the next one), so later calls start clean. Returns DS_OK or
+ * DS_ERR_HIP.
  */
 int ds_query_timeout(hipStream_t stream, int* timed_out);
+
+/*
+ * Testing hook: the next `count` workspace allocations of any entry point
+ * fail with DS_ERR_OUT_OF_MEMORY without calling hipMalloc (count 0 ends
+ * it). The environment variable DEVSCAN_FAIL_ALLOCS=count, read at the first
+ * allocation, does the same. Returns DS_OK or DS_ERR_INVALID_VALUE (count < 0).
+ */
+int ds_fail_next_allocations(int count);
 
 /*
  * Sets the number of polls a look-back wait makes before it gives up
@@ -294,7 +323,7 @@ const char* ds_status_string(int status);
 /* Frees every workspace the library holds, after waiting for the device. */
 void ds_release_workspace(void);
 
-/* Library ABI version (1). */
+/* Library ABI version (2: status values 4-8 renumbered, ds_fail_next_allocations). */
 int ds_version(void);
 
 #ifdef __cplusplus

@@ -20,11 +20,19 @@ DS_INT32, DS_UINT32, DS_FP32, DS_INT64, DS_UINT64 = range(5)
 CMP = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
 ALGO = {"default": 0, "lookback": 1, "three_pass": 2}
 DS_OK = 0
+DS_ERR_INVALID_VALUE = 1
+DS_ERR_UNSUPPORTED_DTYPE = 2
+DS_ERR_OVERLAP = 3
+DS_ERR_OUT_OF_MEMORY = 4
+DS_ERR_HIP = 5
+DS_ERR_MISALIGNED = 6
+DS_ERR_TOO_LARGE = 7
+DS_ERR_STREAM_CAPTURING = 8
 
 EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "ds_scan_seeded", "compact_if", "ds_compact_unordered", "ds_radix_pass",
            "ds_moe_align", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
-           "ds_tile_elems", "ds_scan_tile_elems", "ds_query_timeout", "ds_set_spin_limit", "ds_status_string", "ds_release_workspace",
-           "ds_version"]
+           "ds_tile_elems", "ds_scan_tile_elems", "ds_query_timeout", "ds_fail_next_allocations", "ds_set_spin_limit",
+           "ds_status_string", "ds_release_workspace", "ds_version"]
 TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4,
            "counting_sort": 5, "counting_sort_values": 6, "moe_align": 7}
 TILE_VARIANTS = {"tree": 0, "tree_pad1": 1, "tree_pad2": 2, "hillis_steele": 3}
@@ -59,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ds_tile_pipeline.restype = I
     L.ds_query_timeout.argtypes = [P, ctypes.POINTER(I)]
     L.ds_query_timeout.restype = I
+    L.ds_fail_next_allocations.argtypes = [I]
+    L.ds_fail_next_allocations.restype = I
     L.ds_set_spin_limit.argtypes = [ctypes.c_uint32]
     L.ds_set_spin_limit.restype = I
     L.ds_status_string.argtypes = [I]

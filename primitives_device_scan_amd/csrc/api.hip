@@ -2,6 +2,8 @@
 // the per-(device, stream) workspace, and dispatch to the kernel launchers.
 #include <hip/hip_runtime.h>
 
+#include <stdlib.h>
+
 #include <map>
 #include <mutex>
 #include <utility>
@@ -15,8 +17,8 @@ namespace {
 using ds::Ctrl;
 using ds::DevWs;
 
-// Workspace layout: [Ctrl][status: 16 B per tile][totals: 8 B per tile];
-// `aux` is a separate scratch buffer for the counting-sort tables.
+// Workspace layout: [Ctrl][status: one 128-byte line per tile][totals: 8 B per
+// tile]; `aux` is a separate scratch buffer for the counting-sort tables.
 struct Workspace {
     char* base = nullptr;
     int64_t tile_cap = 0;
@@ -28,22 +30,51 @@ struct Workspace {
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 uint32_t g_spin_limit = 1u << 20;
+int g_fail_allocs = -1;  // workspace allocations still to refuse (testing hook); -1: not read from the environment yet
 
 constexpr uint32_t kDefaultSpin = 1u << 20;
 // Epochs are 30 bits: clear the status words well before one comes round again.
 constexpr uint64_t kEpochClearPeriod = 1ull << 29;
 // Largest n: the grid (tiles x 256 work-items) must stay below 2^32 work-items.
 constexpr int64_t kMaxTiles = ((int64_t)1 << 32) / ds::kThreads - 1;
+constexpr size_t kStatusBytes = (size_t)ds::kStatusWords * sizeof(uint64_t);  // per tile
 
-size_t ws_bytes(int64_t tiles) { return sizeof(Ctrl) + (size_t)tiles * 24; }
+size_t ws_bytes(int64_t tiles) { return sizeof(Ctrl) + (size_t)tiles * (kStatusBytes + 8); }
 
 DevWs view(const Workspace& w)
 {
     DevWs d;
     d.ctrl = reinterpret_cast<Ctrl*>(w.base);
     d.status = reinterpret_cast<uint64_t*>(w.base + sizeof(Ctrl));
-    d.totals = w.base + sizeof(Ctrl) + (size_t)w.tile_cap * 16;
+    d.totals = w.base + sizeof(Ctrl) + (size_t)w.tile_cap * kStatusBytes;
     return d;
+}
+
+// True when `stream` is being captured into a graph: the workspace may then
+// be used but not allocated, grown or cleared (those are not kernel launches).
+bool capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
+// Testing hook: DEVSCAN_FAIL_ALLOCS=k in the environment (read once) or
+// ds_fail_next_allocations(k) makes the next k workspace allocations report
+// DS_ERR_OUT_OF_MEMORY without calling hipMalloc.
+bool refuse_allocation()
+{
+    if (g_fail_allocs < 0) {
+        const char* s = getenv("DEVSCAN_FAIL_ALLOCS");
+        g_fail_allocs = s ? atoi(s) : 0;
+        if (g_fail_allocs < 0) g_fail_allocs = 0;
+    }
+    if (g_fail_allocs == 0) return false;
+    --g_fail_allocs;
+    return true;
 }
 
 // Returns the workspace of (current device, stream) with room for `tiles`;
@@ -53,9 +84,13 @@ int get_workspace(hipStream_t stream, int64_t tiles, Workspace** out)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
     Workspace& w = g_ws[{dev, stream}];
-    if (w.tile_cap < tiles) {
+    const bool grow = w.tile_cap < tiles;
+    const bool clear = w.lookback_launches >= kEpochClearPeriod;
+    if ((grow || clear) && capturing(stream)) return DS_ERR_STREAM_CAPTURING;
+    if (grow) {
         int64_t cap = w.tile_cap * 2 > tiles ? w.tile_cap * 2 : tiles;
         if (cap < 1024) cap = 1024;
+        if (refuse_allocation()) return DS_ERR_OUT_OF_MEMORY;
         if (w.base) {
             // The old buffer may still be in use by work queued on the stream.
             if (hipStreamSynchronize(stream) != hipSuccess) return DS_ERR_HIP;
@@ -77,7 +112,7 @@ int get_workspace(hipStream_t stream, int64_t tiles, Workspace** out)
         w.lookback_launches = 0;
     }
     if (w.lookback_launches >= kEpochClearPeriod) {
-        if (hipMemsetAsync(w.base + sizeof(Ctrl), 0, (size_t)w.tile_cap * 16, stream) != hipSuccess)
+        if (hipMemsetAsync(w.base + sizeof(Ctrl), 0, (size_t)w.tile_cap * kStatusBytes, stream) != hipSuccess)
             return DS_ERR_HIP;
         w.lookback_launches = 0;
     }
@@ -93,8 +128,10 @@ int get_aux(hipStream_t stream, size_t bytes, char** out)
     if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
     Workspace& w = g_ws[{dev, stream}];
     if (w.aux_cap < bytes) {
+        if (capturing(stream)) return DS_ERR_STREAM_CAPTURING;
         size_t cap = w.aux_cap * 2 > bytes ? w.aux_cap * 2 : bytes;
         if (cap < ((size_t)1 << 20)) cap = (size_t)1 << 20;
+        if (refuse_allocation()) return DS_ERR_OUT_OF_MEMORY;
         if (w.aux) {
             if (hipStreamSynchronize(stream) != hipSuccess) return DS_ERR_HIP;
             (void)hipFree(w.aux);
@@ -242,13 +279,8 @@ int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected
     if (n >= ((int64_t)1 << 32)) return DS_ERR_TOO_LARGE;
     int st = check_io(dtype, d_in, d_out, n, true);
     if (st != DS_OK) return st;
-    if (n == 0) {
-        // Nothing to scan: the count is 0, written with a copy from the host.
-        static const int64_t zero = 0;
-        return hipMemcpyAsync(d_num_selected, &zero, sizeof(zero), hipMemcpyHostToDevice, stream) == hipSuccess
-                   ? DS_OK
-                   : DS_ERR_HIP;
-    }
+    if (n == 0)  // nothing to scan: the count is 0, written by a one-thread kernel (capturable)
+        return ds::launch_write_count(d_num_selected, 0, stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
     const int64_t ct = ds::compact_tile_elems(elem_bytes(dtype));
     const int64_t tiles = (n + ct - 1) / ct;
     std::lock_guard<std::mutex> lock(g_mu);
@@ -276,12 +308,8 @@ int ds_compact_unordered(int dtype, const void* d_in, void* d_out, int64_t* d_nu
     if (n >= ((int64_t)1 << 32)) return DS_ERR_TOO_LARGE;
     int st = check_io(dtype, d_in, d_out, n, false);  // out is written in any order: never in place
     if (st != DS_OK) return st;
-    if (n == 0) {
-        static const int64_t zero = 0;
-        return hipMemcpyAsync(d_num_selected, &zero, sizeof(zero), hipMemcpyHostToDevice, stream) == hipSuccess
-                   ? DS_OK
-                   : DS_ERR_HIP;
-    }
+    if (n == 0)  // nothing to scan: the count is 0, written by a one-thread kernel (capturable)
+        return ds::launch_write_count(d_num_selected, 0, stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
     return ds::launch_compact_unordered(kind_of(dtype), d_in, d_out, d_num_selected, n, cmp, operand_bits,
                                         claim == DS_CLAIM_PER_WORKGROUP, stream) == hipSuccess
                ? DS_OK
@@ -344,14 +372,29 @@ int ds_query_timeout(hipStream_t stream, int* timed_out)
     if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
     auto it = g_ws.find({dev, stream});
     if (it == g_ws.end() || !it->second.base) return DS_OK;
-    Ctrl* c = reinterpret_cast<Ctrl*>(it->second.base);
+    Workspace& w = it->second;
+    Ctrl* c = reinterpret_cast<Ctrl*>(w.base);
     uint32_t flag = 0;
     if (hipMemcpy(&flag, &c->timeout, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return DS_ERR_HIP;
     if (flag) {
+        // A wait that gave up may have let the last tile advance the epoch
+        // before slower tiles read it, so their status words can carry the
+        // next launch's epoch. The stream is idle: clear every status word
+        // (and the flag) so the next launch starts from a clean array.
+        if (hipMemset(w.base + sizeof(Ctrl), 0, (size_t)w.tile_cap * kStatusBytes) != hipSuccess) return DS_ERR_HIP;
         const uint32_t zero = 0;
         if (hipMemcpy(&c->timeout, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return DS_ERR_HIP;
+        w.lookback_launches = 0;
     }
     *timed_out = flag ? 1 : 0;
+    return DS_OK;
+}
+
+int ds_fail_next_allocations(int count)
+{
+    if (count < 0) return DS_ERR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_fail_allocs = count;
     return DS_OK;
 }
 
@@ -369,10 +412,13 @@ const char* ds_status_string(int status)
     case DS_ERR_INVALID_VALUE: return "DS_ERR_INVALID_VALUE: bad argument (n < 0, null pointer, bad enum)";
     case DS_ERR_UNSUPPORTED_DTYPE: return "DS_ERR_UNSUPPORTED_DTYPE";
     case DS_ERR_OVERLAP: return "DS_ERR_OVERLAP: input and output partially overlap";
-    case DS_ERR_MISALIGNED: return "DS_ERR_MISALIGNED: pointer not aligned to the element size";
     case DS_ERR_OUT_OF_MEMORY: return "DS_ERR_OUT_OF_MEMORY: workspace allocation failed";
     case DS_ERR_HIP: return "DS_ERR_HIP: a HIP call or kernel launch failed";
+    case DS_ERR_MISALIGNED: return "DS_ERR_MISALIGNED: pointer not aligned to the element size";
     case DS_ERR_TOO_LARGE: return "DS_ERR_TOO_LARGE: n beyond the entry point's limit";
+    case DS_ERR_STREAM_CAPTURING:
+        return "DS_ERR_STREAM_CAPTURING: the workspace would have to be allocated, grown or cleared while the "
+               "stream is being captured (make one call on the stream before capturing)";
     default: return "unknown ds_status";
     }
 }
@@ -480,6 +526,6 @@ int64_t ds_scan_tile_elems(int dtype, int inclusive, int64_t n)
     return ds::tile_elems(kind_of(dtype), inclusive != 0, n);
 }
 
-int ds_version(void) { return 1; }
+int ds_version(void) { return 2; }
 
 }  // extern "C"

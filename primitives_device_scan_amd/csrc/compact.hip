@@ -125,7 +125,22 @@ __global__ __launch_bounds__(kThreads, kCompactOcc) void compact_kernel(const T*
         }
         wave_lds_sync();
     }
-    if (tile == num_tiles - 1 && threadIdx.x == 0) *num_selected = (int64_t)prefix + agg;
+    if (tile == num_tiles - 1 && threadIdx.x == 0) {
+        // -1 when a look-back wait gave up (here or in a tile whose prefix
+        // this one used): the kept elements are then not where they belong.
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const bool bad = !fits || (num_tiles > 1 && __hip_atomic_load(&ctrl->timeout, __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT) != 0u);
+        *num_selected = bad ? (int64_t)-1 : (int64_t)prefix + agg;
+    }
+}
+
+__global__ void write_count_kernel(int64_t* p, int64_t v) { *p = v; }
+
+hipError_t launch_write_count(int64_t* p, int64_t v, hipStream_t stream)
+{
+    write_count_kernel<<<1, 1, 0, stream>>>(p, v);
+    return hipGetLastError();
 }
 
 template <typename T, int CMP>

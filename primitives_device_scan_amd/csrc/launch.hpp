@@ -36,6 +36,9 @@ hipError_t launch_compact(ElemKind kind, const void* in, void* out, int64_t* num
                           int cmp, uint64_t operand_bits, const DevWs& ws, uint32_t spin_limit,
                           hipStream_t stream);
 
+// Writes v to *p with a one-thread kernel (a count when there is nothing to scan).
+hipError_t launch_write_count(int64_t* p, int64_t v, hipStream_t stream);
+
 hipError_t launch_compact_unordered(ElemKind kind, const void* in, void* out, int64_t* count, int64_t n, int cmp,
                                     uint64_t operand_bits, bool per_workgroup, hipStream_t stream);
 

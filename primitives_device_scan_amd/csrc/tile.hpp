@@ -332,9 +332,17 @@ __device__ __forceinline__ void tile_finish(T (&e)[V * VPT], const T (&off)[VPT]
 // Words are written and read with relaxed device-scope atomics: coherent
 // across the XCDs' separate L2 caches, with no cache writeback or invalidate.
 // Each word carries its own value, so no ordering with other memory is needed.
+//
+// Each tile's words sit alone in one 128-byte line (kStatusWords 64-bit words
+// per tile; an 8-byte value uses the first two). Packed eight to a line, the
+// words of neighbouring tiles share a line that is written by one tile while
+// the next polls it; measured on MI355X at n = 100M int32, padding each tile
+// to its own line makes the whole scan 3-4% faster (144 -> 139 us), although
+// a 64-tile window read then touches 64 lines instead of 4.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kFlagNone = 0, kFlagAggregate = 1, kFlagPrefix = 2;
 constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
+constexpr int kStatusWords = 16;  // 64-bit words (one 128-byte line) per tile
 
 __device__ __forceinline__ void status_store(uint64_t* p, uint64_t w)
 {
@@ -353,31 +361,32 @@ __device__ __forceinline__ uint64_t status_word(uint32_t epoch, uint32_t flag, u
 
 template <typename T>
 struct StatusCodec {
-    static constexpr int kWords = sizeof(T) / 4;  // 64-bit words per tile
 
     static __device__ __forceinline__ void publish(uint64_t* status, int64_t tile, uint32_t epoch,
                                                    uint32_t flag, T v)
     {
+        uint64_t* p = status + tile * kStatusWords;
         if constexpr (sizeof(T) == 4) {
-            status_store(status + tile, status_word(epoch, flag, __builtin_bit_cast(uint32_t, v)));
+            status_store(p, status_word(epoch, flag, __builtin_bit_cast(uint32_t, v)));
         } else {
             const uint64_t u = __builtin_bit_cast(uint64_t, v);
-            status_store(status + 2 * tile, status_word(epoch, flag, (uint32_t)u));
-            status_store(status + 2 * tile + 1, status_word(epoch, flag, (uint32_t)(u >> 32)));
+            status_store(p, status_word(epoch, flag, (uint32_t)u));
+            status_store(p + 1, status_word(epoch, flag, (uint32_t)(u >> 32)));
         }
     }
 
     // Reads tile `idx`'s status; returns its flag (kFlagNone when stale or torn).
     static __device__ __forceinline__ uint32_t read(uint64_t* status, int64_t idx, uint32_t epoch, T& v)
     {
+        uint64_t* p = status + idx * kStatusWords;
         if constexpr (sizeof(T) == 4) {
-            const uint64_t w = status_load(status + idx);
+            const uint64_t w = status_load(p);
             const uint32_t hi = (uint32_t)(w >> 32);
             v = __builtin_bit_cast(T, (uint32_t)w);
             return (hi >> 2) == epoch ? (hi & 3u) : kFlagNone;
         } else {
-            const uint64_t w0 = status_load(status + 2 * idx);
-            const uint64_t w1 = status_load(status + 2 * idx + 1);
+            const uint64_t w0 = status_load(p);
+            const uint64_t w1 = status_load(p + 1);
             const uint32_t h0 = (uint32_t)(w0 >> 32), h1 = (uint32_t)(w1 >> 32);
             v = __builtin_bit_cast(T, (uint64_t)(uint32_t)w0 | (w1 << 32));
             return (h0 == h1 && (h0 >> 2) == epoch) ? (h0 & 3u) : kFlagNone;
@@ -411,6 +420,8 @@ __device__ T lookback(uint64_t* status, int64_t tile, uint32_t epoch, T agg, uin
     auto give_up = [&]() {
         gave_up = true;
         if (lane == 0) __hip_atomic_store(timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the flag becomes visible before the (incomplete) prefix this tile publishes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     };
     for (;;) {
         uint32_t f = kFlagPrefix;

@@ -70,6 +70,7 @@ def gpu_scan(x: np.ndarray, inclusive: bool, algo: str = "default", in_place: bo
         st = f(CODE[x.dtype], pin, pout, n, stream_handle())
     assert st == 0, ds.lib.ds_status_string(st)
     torch.cuda.synchronize()
+    assert ds.query_timeout() is False, "a look-back wait gave up: the output is not valid"
     return from_dev(out, x.dtype, offset, n)
 
 
@@ -91,6 +92,7 @@ def gpu_compact(x: np.ndarray, op: str, operand, in_place: bool = False, offset:
                            cnt.data_ptr(), n, ds.CMP[op], bits, stream_handle())
     assert st == 0, ds.lib.ds_status_string(st)
     torch.cuda.synchronize()
+    assert ds.query_timeout() is False, "a look-back wait gave up: the output is not valid"
     k = int(cnt.item())
     return from_dev(out, x.dtype, offset, n), k
 

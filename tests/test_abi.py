@@ -46,10 +46,33 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ds_version() == 1
-    for s in range(8):
+    assert lib.ds_version() == 2
+    for s in range(9):
         assert lib.ds_status_string(s).startswith(b"DS_")
     assert b"unknown" in lib.ds_status_string(99)
+
+
+# ds_status values (include/devscan.h)
+OK, INV, DTY, OVL, OOM, HIPERR, MIS, BIG, CAPT = range(9)
+
+
+def test_status_values_match_the_header():
+    """The binding's constants are the header's enum, value by value."""
+    from primitives_device_scan_amd import _binding
+    text = open(os.path.join(ROOT, "include", "devscan.h")).read()
+    enum = text[text.index("DS_OK = 0"):text.index("} ds_status;")]
+    pairs = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"(DS_[A-Z_]+)\s*=\s*(\d+)", enum))
+    assert pairs["DS_ERR_OUT_OF_MEMORY"] == 4 and pairs["DS_ERR_HIP"] == 5
+    for name, value in pairs.items():
+        assert getattr(_binding, name) == value, name
+    assert [OK, INV, DTY, OVL, OOM, HIPERR, MIS, BIG, CAPT] == [pairs[k] for k in (
+        "DS_OK", "DS_ERR_INVALID_VALUE", "DS_ERR_UNSUPPORTED_DTYPE", "DS_ERR_OVERLAP", "DS_ERR_OUT_OF_MEMORY",
+        "DS_ERR_HIP", "DS_ERR_MISALIGNED", "DS_ERR_TOO_LARGE", "DS_ERR_STREAM_CAPTURING")]
+
+
+def test_fail_next_allocations_arguments(lib):
+    assert lib.ds_fail_next_allocations(-1) == INV
+    assert lib.ds_fail_next_allocations(0) == OK
 
 
 # Fake, never-dereferenced addresses: validation must reject these on the host.
@@ -60,111 +83,111 @@ B = 0x7F0000100000
 @pytest.mark.parametrize("fn", ["scan_exclusive", "scan_inclusive"])
 def test_scan_validation(lib, fn):
     f = getattr(lib, fn)
-    assert f(7, A, B, 10, None) == 2            # DS_ERR_UNSUPPORTED_DTYPE
-    assert f(-1, A, B, 10, None) == 2
-    assert f(0, A, B, -1, None) == 1            # n < 0
-    assert f(0, None, B, 10, None) == 1         # null with n > 0
-    assert f(0, A, None, 10, None) == 1
-    assert f(0, None, None, 0, None) == 0       # n == 0: nothing to do, no launch
-    assert f(0, A, A + 4, 10, None) == 3        # partial overlap
-    assert f(0, A + 4, A, 10, None) == 3
-    assert f(0, A + 2, B, 10, None) == 4        # misaligned for int32
-    assert f(3, A + 4, B, 10, None) == 4        # misaligned for int64
-    assert f(0, A, B, 1 << 40, None) == 7       # beyond the grid limit
+    assert f(7, A, B, 10, None) == DTY            # DS_ERR_UNSUPPORTED_DTYPE
+    assert f(-1, A, B, 10, None) == DTY
+    assert f(0, A, B, -1, None) == INV            # n < 0
+    assert f(0, None, B, 10, None) == INV         # null with n > 0
+    assert f(0, A, None, 10, None) == INV
+    assert f(0, None, None, 0, None) == OK       # n == 0: nothing to do, no launch
+    assert f(0, A, A + 4, 10, None) == OVL        # partial overlap
+    assert f(0, A + 4, A, 10, None) == OVL
+    assert f(0, A + 2, B, 10, None) == MIS        # misaligned for int32
+    assert f(3, A + 4, B, 10, None) == MIS        # misaligned for int64
+    assert f(0, A, B, 1 << 40, None) == BIG       # beyond the grid limit
 
 
 def test_ds_scan_validation(lib):
-    assert lib.ds_scan(0, 2, 0, A, B, 10, None) == 1   # inclusive not 0/1
-    assert lib.ds_scan(0, 0, 3, A, B, 10, None) == 1   # bad algo
-    assert lib.ds_scan(0, 0, -1, A, B, 10, None) == 1
-    assert lib.ds_scan(2, 1, 2, A, A + 8, 10, None) == 3
+    assert lib.ds_scan(0, 2, 0, A, B, 10, None) == INV   # inclusive not 0/1
+    assert lib.ds_scan(0, 0, 3, A, B, 10, None) == INV   # bad algo
+    assert lib.ds_scan(0, 0, -1, A, B, 10, None) == INV
+    assert lib.ds_scan(2, 1, 2, A, A + 8, 10, None) == OVL
 
 
 def test_scan_seeded_validation(lib):
     f = lib.ds_scan_seeded
     S = 0x7F0000200000
-    assert f(7, 0, A, B, 10, S, None) == 2         # DS_ERR_UNSUPPORTED_DTYPE
-    assert f(0, 2, A, B, 10, S, None) == 1         # inclusive not 0/1
-    assert f(0, 0, A, B, -1, S, None) == 1
-    assert f(0, 0, None, None, 0, S, None) == 0    # n == 0: nothing to do
-    assert f(0, 0, A, B, 10, S + 2, None) == 4     # seed misaligned for int32
-    assert f(3, 0, A, B, 10, S + 4, None) == 4     # ... and for int64
-    assert f(0, 0, A, B, 10, B + 8, None) == 3     # seed inside the output
-    assert f(0, 0, A, A + 4, 10, S, None) == 3     # partial overlap of in and out
-    assert f(0, 0, A, B, 1 << 40, S, None) == 7
+    assert f(7, 0, A, B, 10, S, None) == DTY         # DS_ERR_UNSUPPORTED_DTYPE
+    assert f(0, 2, A, B, 10, S, None) == INV         # inclusive not 0/1
+    assert f(0, 0, A, B, -1, S, None) == INV
+    assert f(0, 0, None, None, 0, S, None) == OK    # n == 0: nothing to do
+    assert f(0, 0, A, B, 10, S + 2, None) == MIS     # seed misaligned for int32
+    assert f(3, 0, A, B, 10, S + 4, None) == MIS     # ... and for int64
+    assert f(0, 0, A, B, 10, B + 8, None) == OVL     # seed inside the output
+    assert f(0, 0, A, A + 4, 10, S, None) == OVL     # partial overlap of in and out
+    assert f(0, 0, A, B, 1 << 40, S, None) == BIG
 
 
 def test_compact_validation(lib):
     C = 0x7F0000200000
-    assert lib.compact_if(9, A, B, C, 10, 0, 0, None) == 2
-    assert lib.compact_if(0, A, B, C, 10, 6, 0, None) == 1   # bad cmp
-    assert lib.compact_if(0, A, B, C, 10, -1, 0, None) == 1
-    assert lib.compact_if(0, A, B, None, 10, 0, 0, None) == 1
-    assert lib.compact_if(0, A, B, C, -3, 0, 0, None) == 1
-    assert lib.compact_if(0, A, B, C + 4, 10, 0, 0, None) == 4
-    assert lib.compact_if(0, A, B, C, 1 << 32, 0, 0, None) == 7
-    assert lib.compact_if(0, A, A + 4, C, 10, 0, 0, None) == 3
-    assert lib.compact_if(0, None, B, C, 10, 0, 0, None) == 1
+    assert lib.compact_if(9, A, B, C, 10, 0, 0, None) == DTY
+    assert lib.compact_if(0, A, B, C, 10, 6, 0, None) == INV   # bad cmp
+    assert lib.compact_if(0, A, B, C, 10, -1, 0, None) == INV
+    assert lib.compact_if(0, A, B, None, 10, 0, 0, None) == INV
+    assert lib.compact_if(0, A, B, C, -3, 0, 0, None) == INV
+    assert lib.compact_if(0, A, B, C + 4, 10, 0, 0, None) == MIS
+    assert lib.compact_if(0, A, B, C, 1 << 32, 0, 0, None) == BIG
+    assert lib.compact_if(0, A, A + 4, C, 10, 0, 0, None) == OVL
+    assert lib.compact_if(0, None, B, C, 10, 0, 0, None) == INV
 
 
 def test_compact_unordered_validation(lib):
     C = 0x7F0000200000
     f = lib.ds_compact_unordered
-    assert f(9, A, B, C, 10, 0, 0, 0, None) == 2
-    assert f(0, A, B, C, 10, 6, 0, 0, None) == 1     # bad cmp
-    assert f(0, A, B, C, 10, 0, 0, 2, None) == 1     # bad claim
-    assert f(0, A, B, C, 10, 0, 0, -1, None) == 1
-    assert f(0, A, B, None, 10, 0, 0, 1, None) == 1
-    assert f(0, A, B, C, -3, 0, 0, 1, None) == 1
-    assert f(0, A, B, C + 4, 10, 0, 0, 1, None) == 4
-    assert f(0, A, B, C, 1 << 32, 0, 0, 1, None) == 7
-    assert f(0, A, A, C, 10, 0, 0, 1, None) == 3     # never in place: the order is not kept
-    assert f(0, A, A + 4, C, 10, 0, 0, 0, None) == 3
-    assert f(0, None, B, C, 10, 0, 0, 0, None) == 1
+    assert f(9, A, B, C, 10, 0, 0, 0, None) == DTY
+    assert f(0, A, B, C, 10, 6, 0, 0, None) == INV     # bad cmp
+    assert f(0, A, B, C, 10, 0, 0, 2, None) == INV     # bad claim
+    assert f(0, A, B, C, 10, 0, 0, -1, None) == INV
+    assert f(0, A, B, None, 10, 0, 0, 1, None) == INV
+    assert f(0, A, B, C, -3, 0, 0, 1, None) == INV
+    assert f(0, A, B, C + 4, 10, 0, 0, 1, None) == MIS
+    assert f(0, A, B, C, 1 << 32, 0, 0, 1, None) == BIG
+    assert f(0, A, A, C, 10, 0, 0, 1, None) == OVL     # never in place: the order is not kept
+    assert f(0, A, A + 4, C, 10, 0, 0, 0, None) == OVL
+    assert f(0, None, B, C, 10, 0, 0, 0, None) == INV
 
 
 def test_radix_pass_validation(lib):
     f = lib.ds_radix_pass
     C, D = 0x7F0000200000, 0x7F0000300000
-    assert f(A, B, None, None, 10, 0, 0, None) == 1      # bits 0
-    assert f(A, B, None, None, 10, 0, 9, None) == 1      # bits 9
-    assert f(A, B, None, None, 10, -1, 8, None) == 1
-    assert f(A, B, None, None, 10, 32, 1, None) == 1
-    assert f(A, B, None, None, 10, 28, 8, None) == 1     # shift + bits > 32
-    assert f(A, B, C, None, 10, 0, 8, None) == 1         # values in without values out
-    assert f(A, B, None, None, -1, 0, 8, None) == 1
-    assert f(None, None, None, None, 0, 0, 8, None) == 0  # n == 0: nothing to do
-    assert f(A, B, None, None, 1 << 32, 0, 8, None) == 7
-    assert f(None, B, None, None, 10, 0, 8, None) == 1
-    assert f(A + 2, B, None, None, 10, 0, 8, None) == 4
-    assert f(A, B, C + 2, D, 10, 0, 8, None) == 4
-    assert f(A, A, None, None, 10, 0, 8, None) == 3      # never in place
-    assert f(A, A + 8, None, None, 10, 0, 8, None) == 3
-    assert f(A, B, C, B + 4, 10, 0, 8, None) == 3        # values out over keys out
+    assert f(A, B, None, None, 10, 0, 0, None) == INV      # bits 0
+    assert f(A, B, None, None, 10, 0, 9, None) == INV      # bits 9
+    assert f(A, B, None, None, 10, -1, 8, None) == INV
+    assert f(A, B, None, None, 10, 32, 1, None) == INV
+    assert f(A, B, None, None, 10, 28, 8, None) == INV     # shift + bits > 32
+    assert f(A, B, C, None, 10, 0, 8, None) == INV         # values in without values out
+    assert f(A, B, None, None, -1, 0, 8, None) == INV
+    assert f(None, None, None, None, 0, 0, 8, None) == OK  # n == 0: nothing to do
+    assert f(A, B, None, None, 1 << 32, 0, 8, None) == BIG
+    assert f(None, B, None, None, 10, 0, 8, None) == INV
+    assert f(A + 2, B, None, None, 10, 0, 8, None) == MIS
+    assert f(A, B, C + 2, D, 10, 0, 8, None) == MIS
+    assert f(A, A, None, None, 10, 0, 8, None) == OVL      # never in place
+    assert f(A, A + 8, None, None, 10, 0, 8, None) == OVL
+    assert f(A, B, C, B + 4, 10, 0, 8, None) == OVL        # values out over keys out
 
 
 def test_moe_align_validation(lib):
     f = lib.ds_moe_align
     C, D, E = 0x7F0000200000, 0x7F0000300000, 0x7F0000400000
-    assert f(A, 100, 0, 64, B, C, D, 10000, None) == 1     # no experts
-    assert f(A, 100, 512, 64, B, C, D, 100000, None) == 1  # more experts than buckets
-    assert f(A, 100, 8, 0, B, C, D, 10000, None) == 1      # block 0
-    assert f(A, -1, 8, 64, B, C, D, 10000, None) == 1
-    assert f(A, 100, 8, 64, None, C, D, 10000, None) == 1
-    assert f(None, 100, 8, 64, B, C, D, 10000, None) == 1
-    assert f(A, 100, 8, 64, B, C, D, 100 + 8 * 63 - 1, None) == 1   # capacity below the worst case
-    assert f(A, 1 << 31, 8, 64, B, C, D, 1 << 32, None) == 7
-    assert f(A + 2, 100, 8, 64, B, C, D, 10000, None) == 4
-    assert f(A, 100, 8, 64, B, C, A + 200, 10000, None) == 3        # sorted ids over the input
-    assert f(A, 100, 8, 64, B, B + 16, D, 10000, None) == 3         # offsets over counts
+    assert f(A, 100, 0, 64, B, C, D, 10000, None) == INV     # no experts
+    assert f(A, 100, 512, 64, B, C, D, 100000, None) == INV  # more experts than buckets
+    assert f(A, 100, 8, 0, B, C, D, 10000, None) == INV      # block 0
+    assert f(A, -1, 8, 64, B, C, D, 10000, None) == INV
+    assert f(A, 100, 8, 64, None, C, D, 10000, None) == INV
+    assert f(None, 100, 8, 64, B, C, D, 10000, None) == INV
+    assert f(A, 100, 8, 64, B, C, D, 100 + 8 * 63 - 1, None) == INV   # capacity below the worst case
+    assert f(A, 1 << 31, 8, 64, B, C, D, 1 << 32, None) == BIG
+    assert f(A + 2, 100, 8, 64, B, C, D, 10000, None) == MIS
+    assert f(A, 100, 8, 64, B, C, A + 200, 10000, None) == OVL        # sorted ids over the input
+    assert f(A, 100, 8, 64, B, B + 16, D, 10000, None) == OVL         # offsets over counts
 
 
 def test_copy_validation(lib):
-    assert lib.ds_copy(A, B, 17, None) == 1
-    assert lib.ds_copy(A, B, -16, None) == 1
-    assert lib.ds_copy(A, B, 0, None) == 0
-    assert lib.ds_copy(A + 4, B, 32, None) == 4
-    assert lib.ds_copy(A, A + 16, 64, None) == 3
+    assert lib.ds_copy(A, B, 17, None) == INV
+    assert lib.ds_copy(A, B, -16, None) == INV
+    assert lib.ds_copy(A, B, 0, None) == OK
+    assert lib.ds_copy(A + 4, B, 32, None) == MIS
+    assert lib.ds_copy(A, A + 16, 64, None) == OVL
 
 
 def test_tile_queries(lib):
@@ -173,7 +196,7 @@ def test_tile_queries(lib):
     # the counting-sort tiles exist for 4-byte keys only
     for entry in _binding.TILE_OF.values():
         t = lib.ds_tile_elems(1, entry)
-        assert t > 0 and t % 256 == 0, (entry, t)
+        assert t > 0 and t % 256 == OK, (entry, t)
     for name in ("counting_sort", "counting_sort_values", "moe_align", "lds_tile_scan"):
         assert lib.ds_tile_elems(3, _binding.TILE_OF[name]) == -1, name
     assert lib.ds_tile_elems(1, max(_binding.TILE_OF.values()) + 1) == -1
@@ -181,12 +204,12 @@ def test_tile_queries(lib):
     assert lib.ds_tile_elems(9, 0) == -1
     for n in (0, 1, 4096, 1 << 20, 1 << 23, 100_000_007):
         t = lib.ds_scan_tile_elems(1, 0, n)
-        assert t > 0 and t % 256 == 0, (n, t)
+        assert t > 0 and t % 256 == OK, (n, t)
     assert lib.ds_scan_tile_elems(1, 2, 10) == -1 and lib.ds_scan_tile_elems(1, 0, -1) == -1
 
 
 def test_query_timeout_null(lib):
-    assert lib.ds_query_timeout(None, None) == 1
+    assert lib.ds_query_timeout(None, None) == INV
 
 
 def test_binding_refuses_a_missing_library(tmp_path):

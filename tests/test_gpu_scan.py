@@ -11,8 +11,8 @@ import torch
 import datagen
 import oracle
 import pins
-from gpu_util import (assert_fp32_close, assert_int_equal, cached_workload, check_scan, gpu_scan, say, scan_tile,
-                      tile_of)
+from gpu_util import (assert_fp32_close, assert_int_equal, cached_workload, check_scan, gpu_compact, gpu_scan, say,
+                      scan_tile, stream_handle, tile_of, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -288,21 +288,38 @@ def test_binding_entry_points():
 
 def test_give_up_path_then_recovery():
     """A tiny spin limit makes look-back waits give up (outputs invalid, flag
-    set) while every kernel still finishes; later calls are correct again."""
+    set) while every kernel still finishes; compact_if then writes -1 as its
+    count; after ds_query_timeout (which clears the status words) later calls
+    are correct again."""
+    import torch
+
     import primitives_device_scan_amd as ds
     n = 300 * tile_of(np.int32) + 9
     x = datagen.uniform_int(5, n, 0, 9)
-    ds.query_timeout()  # clear
+    xin = to_dev(x)
+    out = torch.empty_like(xin)
+    cnt = torch.full((1,), -7, dtype=torch.int64, device="cuda")
+    h = stream_handle()
+    assert ds.query_timeout() is False
     ds.set_spin_limit(1)
     try:
         for _ in range(3):
-            gpu_scan(x, False)
+            assert ds.lib.ds_scan(0, 0, 0, xin.data_ptr(), out.data_ptr(), n, h) == 0
         gave_up = ds.query_timeout()
-        say(f"spin limit 1: gave up = {gave_up}")
+        say(f"spin limit 1, scans: gave up = {gave_up}")
+        assert ds.lib.compact_if(0, xin.data_ptr(), out.data_ptr(), cnt.data_ptr(), n, ds.CMP[">"], 4, h) == 0
+        gave_up_c = ds.query_timeout()
+        k = int(cnt.item())
+        say(f"spin limit 1, compact_if: gave up = {gave_up_c}, count = {k}")
+        want_k = int(np.count_nonzero(x > 4))
+        assert k == -1 if gave_up_c else k == want_k
     finally:
         ds.set_spin_limit(0)
     for _ in range(3):
         check_scan(x, False, gpu_scan(x, False), "after give-up")
+    got, k = gpu_compact(x, ">", 4)
+    want = oracle.compact(x, ">", 4)
+    assert k == want.size and np.array_equal(got[:k], want)
     assert ds.query_timeout() is False
 
 
