@@ -7,21 +7,33 @@ One step = the exclusive scan of 100,000,007 int32 values (uniform in
 libdevscan.so (one look-back kernel launch each). Inputs are synthetic and
 seeded (datagen). Prints one JSON line:
 
-  value      whole-job G-elem/s = 2 * n * steps / timed seconds
-  roofline   the look-back scan kernel against MI355X peak HBM bandwidth:
-             algorithmic bytes 2 * n * 4 per launch / mean launch time from
-             HIP events on the launch stream
+  value      whole-job G-elem/s = 2 * n * steps / timed seconds (the K steps
+             run back to back)
+  roofline   the look-back scan kernel against MI355X peak HBM bandwidth,
+             algorithmic bytes 2 * n * 4 per launch:
+               frac / achieved  cold: the median of 50 launches of each scan,
+                                each after a 1 GiB read that evicts L2 and the
+                                memory-side cache (HIP events on the launch
+                                stream)
+               frac_warm / achieved_warm  the mean launch time over the timed
+                                back-to-back steps
   cpu_baseline  the sequential CPU oracle on the host, same inputs (extras
              also carry a second CPU row: a two-pass blocked scan on up to
              16 host threads)
-  extras     the same-pattern copy, the three-pass scan, cold-cache scans,
-             the other workloads' scans (one tile, 1M int32, fp32 10M
-             inclusive, int64 100M), the small ones also replayed from a HIP
-             graph, and (unless --no-compact / --no-sort)
-             compaction of 268,435,456
-             uint32 keys (ordered and both unordered forms), one 8-bit
-             counting-sort pass over those keys (with and without values) and
-             MoE alignment of two router workloads
+  extras     the same-pattern copy, the three-pass scan, the other
+             workloads' scans (one tile, 1M int32, fp32 10M inclusive, int64
+             100M), the small ones also replayed from a HIP graph, and
+             (unless --no-compact / --no-sort) compaction of 268,435,456
+             uint32 keys (ordered, against its read-all / write-half ceiling,
+             and both unordered forms), one 8-bit counting-sort pass over
+             those keys (with and without values) and MoE alignment of two
+             router workloads
+
+Other modes (their own JSON line): --ceiling (the access-pattern table:
+read, write, copy and read-all/write-half at 4 to 112 KiB per workgroup,
+contiguous and 4 KiB-interleaved, warm and cold), --tile-lds (the pages' LDS
+block-scan experiment), --profile-only [--cold] [--pattern ...] (launches
+without timing, for rocprofv3).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-compact] [--no-sort]
 """
@@ -66,6 +78,36 @@ def kernel_source_sha() -> str:
     for p in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
+
+
+class Evictor:
+    """Evicts L2 and the memory-side cache before a cold launch: reads a 1 GiB
+    scratch buffer (a reduction, so the lines it leaves behind are clean and
+    the next launch writes nothing back), then waits for the device."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.sink = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.sink += self.buf.sum()  # one reduction kernel: reads 1 GiB, writes a few bytes
+        self.torch.cuda.synchronize()
+
+
+def cold_times_ms(torch, stream, fn, evict, reps=50):
+    """Launch times (ms, HIP events on `stream`) of `reps` launches of fn, each
+    after evict()."""
+    out = []
+    for _ in range(reps):
+        evict()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
 
 
 def measured_traffic(per_launch_alg_bytes: float):
@@ -184,6 +226,106 @@ def tile_lds_experiment(args):
                       "lookback_scan_us_same_input": round(lb_ms * 1e3, 1)}), flush=True)
 
 
+def ceiling_experiment(args):
+    """The access-pattern table the scan and the compaction are read against:
+    ds_bandwidth_pattern for read / write / copy / read-all-write-half at 4,
+    16, 64 and 112 KiB per workgroup, contiguous tiles (the scan's layout) and
+    4 KiB chunks at a 32 KiB stride, on 400,000,016 bytes per buffer (the
+    100M-element scan's input); plus ds_copy (the scan's own tile) and
+    compact_if's read-all-write-half pattern at its 64 KiB tile on 1 GiB.
+    Warm: median of 10 back-to-back launches; cold: median of 10 launches each
+    after a 1 GiB read."""
+    import numpy as np
+    import torch
+
+    import primitives_device_scan_amd as ds
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    L = ds.lib
+    nbytes = 100_000_007 * 4 // 16 * 16
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.zeros_like(a)
+    evict = Evictor(torch, dev)
+
+    def warm_ms(fn, reps=10):
+        for _ in range(2):
+            fn()
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for x, y in es:
+            x.record(stream)
+            fn()
+            y.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([x.elapsed_time(y) for x, y in es]))
+
+    rows = []
+    for mode, mcode in ds._binding.PATTERNS.items():
+        moved = {"read": 1.0, "write": 1.0, "copy": 2.0, "read_half": 1.5}[mode]
+        for vpt in (1, 4, 16, 28):
+            for layout in (0, 1):
+                def fn():
+                    st = L.ds_bandwidth_pattern(mcode, vpt, layout, a.data_ptr(), b.data_ptr(), nbytes, sh)
+                    if st:
+                        raise ds.DevscanError(st, "ds_bandwidth_pattern")
+                w = warm_ms(fn)
+                c = float(np.median(cold_times_ms(torch, stream, fn, evict, reps=10)))
+                row = {"mode": mode, "kib_per_workgroup": 4 * vpt,
+                       "layout": "contiguous" if layout == 0 else "4KiB_chunks_32KiB_stride",
+                       "warm_us": round(w * 1e3, 1), "warm_gbs": round(moved * nbytes / (w * 1e-3) / 1e9, 1),
+                       "cold_us": round(c * 1e3, 1), "cold_gbs": round(moved * nbytes / (c * 1e-3) / 1e9, 1)}
+                rows.append(row)
+                log(f"{mode:9s} {4 * vpt:4d} KiB/WG {row['layout']:24s} warm {row['warm_us']:7.1f} us "
+                    f"{row['warm_gbs']:7.1f} GB/s  cold {row['cold_us']:7.1f} us {row['cold_gbs']:7.1f} GB/s")
+    cp = lambda: L.ds_copy(a.data_ptr(), b.data_ptr(), nbytes, sh)
+    cw, cc = warm_ms(cp), float(np.median(cold_times_ms(torch, stream, cp, evict, reps=10)))
+    out = {"mode": "ceiling", "bytes_per_buffer": nbytes, "peak_gbs": PEAK_HBM_GBS, "rows": rows,
+           "ds_copy_scan_tile": {"kib_per_workgroup": int(L.ds_tile_elems(ds.DS_INT32, 0)) * 4 // 1024,
+                                 "warm_us": round(cw * 1e3, 1), "cold_us": round(cc * 1e3, 1),
+                                 "warm_gbs": round(2 * nbytes / (cw * 1e-3) / 1e9, 1),
+                                 "cold_gbs": round(2 * nbytes / (cc * 1e-3) / 1e9, 1)}}
+    del a, b
+    # compaction's own shape: 2^28 uint32 keys, its 64 KiB tile, half written
+    nk = 1 << 28
+    keys = torch.ones(nk, dtype=torch.int32, device=dev)
+    kout = torch.zeros_like(keys)
+    cvpt = int(L.ds_tile_elems(ds.DS_UINT32, ds._binding.TILE_OF["compact"])) // 1024
+    hf = lambda: L.ds_bandwidth_pattern(3, cvpt, 0, keys.data_ptr(), kout.data_ptr(), nk * 4, sh)
+    hw, hc = warm_ms(hf), float(np.median(cold_times_ms(torch, stream, hf, evict, reps=10)))
+    out["compaction_shape_256m"] = {"kib_per_workgroup": 4 * cvpt, "bytes": int(nk * 6),
+                                    "warm_us": round(hw * 1e3, 1), "cold_us": round(hc * 1e3, 1)}
+    print(json.dumps(out), flush=True)
+
+
+def profile_pattern(args):
+    """--profile-only --pattern MODE:VPT:LAYOUT: --steps launches of one
+    ds_bandwidth_pattern case on 400,000,016-byte buffers (each after a 1 GiB
+    read with --cold), for counter runs."""
+    import torch
+
+    import primitives_device_scan_amd as ds
+
+    mode, vpt, layout = args.pattern.split(":")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    nbytes = 100_000_007 * 4 // 16 * 16
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.zeros_like(a)
+    evict = Evictor(torch, dev) if args.cold else (lambda: None)
+    for _ in range(max(1, args.steps)):
+        evict()
+        st = ds.lib.ds_bandwidth_pattern(ds._binding.PATTERNS[mode], int(vpt), int(layout), a.data_ptr(),
+                                         b.data_ptr(), nbytes, sh)
+        if st:
+            raise ds.DevscanError(st, "ds_bandwidth_pattern")
+    torch.cuda.synchronize()
+    log(f"profile run done: {args.pattern} x {args.steps}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +344,13 @@ def main():
     ap.add_argument("--no-check", action="store_true", help="with --profile-only: skip the oracle check")
     ap.add_argument("--tile-lds", action="store_true",
                     help="the pages' LDS block-scan experiment instead of the main bench (own JSON line)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="the access-pattern ceiling table instead of the main bench (own JSON line)")
+    ap.add_argument("--cold", action="store_true",
+                    help="with --profile-only: a 1 GiB read before every scan launch (the cold protocol)")
+    ap.add_argument("--pattern", default=None,
+                    help="with --profile-only: MODE:VPT:LAYOUT of ds_bandwidth_pattern to launch --steps times "
+                         "instead of the scans (e.g. write:28:0)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -212,6 +361,10 @@ def main():
 
     if args.tile_lds:
         return tile_lds_experiment(args)
+    if args.ceiling:
+        return ceiling_experiment(args)
+    if args.profile_only and args.pattern:
+        return profile_pattern(args)
 
     import numpy as np
     import torch
@@ -264,10 +417,15 @@ def main():
         # Scans, then the same-pattern copy of a known size (n*4 bytes read,
         # n*4 bytes written per launch; n*4 rounded down to 16 bytes), whose
         # counters give the scale factor for the scans' FETCH/WRITE_SIZE.
+        # --cold: each launch (scans and copies) after a 1 GiB read.
+        evict = Evictor(torch, dev) if args.cold else (lambda: None)
         for _ in range(K):
+            evict()
             scan_i()
+            evict()
             scan_f()
         for _ in range(K):
+            evict()
             st = L.ds_copy(d_xi.data_ptr(), d_yi.data_ptr(), n * 4 // 16 * 16, sh)
             if st:
                 raise ds.DevscanError(st, "ds_copy")
@@ -329,25 +487,23 @@ def main():
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in es]))
 
-    # Cold caches: a 1 GiB fill between launches evicts L2 and the memory-side
-    # cache; the timed value above is the back-to-back (warm) rate.
-    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    # Cold caches (the headline): 50 launches of each scan, each after a 1 GiB
+    # read that evicts L2 and the memory-side cache; medians.
+    evict = Evictor(torch, dev)
+    cold = {}
     for name, fn in (("int32", scan_i), ("fp32", scan_f)):
-        cold = []
-        for r in range(10):
-            flush.fill_(r)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            cold.append(a.elapsed_time(b))
-        extras[f"{name}_excl_cold_us_median"] = round(float(np.median(cold)) * 1e3, 2)
-    del flush
+        cold[name] = cold_times_ms(torch, stream, fn, evict, reps=50)
+        extras[f"{name}_excl_cold_us_median"] = round(float(np.median(cold[name])) * 1e3, 2)
+        extras[f"{name}_excl_cold_us_p10_p90"] = [round(float(np.percentile(cold[name], q)) * 1e3, 2) for q in (10, 90)]
+    cold_ms = float(np.median(cold["int32"] + cold["fp32"]))
 
-    cp_ms = timed(lambda: L.ds_copy(d_xi.data_ptr(), d_yi.data_ptr(), n * 4 // 16 * 16, sh))
+    cpf = lambda: L.ds_copy(d_xi.data_ptr(), d_yi.data_ptr(), n * 4 // 16 * 16, sh)
+    cp_ms = timed(cpf)
+    cp_cold_ms = float(np.median(cold_times_ms(torch, stream, cpf, evict, reps=20)))
     extras["copy_same_pattern_gbs"] = round(alg_bytes / (cp_ms * 1e-3) / 1e9, 1)
+    extras["copy_same_pattern_cold_gbs"] = round(alg_bytes / (cp_cold_ms * 1e-3) / 1e9, 1)
     extras["scan_over_copy"] = round(cp_ms / float(np.median(ms_i)), 4)
+    extras["scan_over_copy_cold"] = round(cp_cold_ms / cold_ms, 4)
     tp_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 0, ds.ALGO["three_pass"], d_xi.data_ptr(), d_yi.data_ptr(), n, sh))
     extras["three_pass_int32_gelem_s"] = round(n / (tp_ms * 1e-3) / 1e9, 2)
     extras["three_pass_int32_alg_gbs"] = round(alg_bytes / (tp_ms * 1e-3) / 1e9, 1)
@@ -423,6 +579,11 @@ def main():
         kept = int(cnt.item())
         cbytes = nk * 4 + kept * 4
         extras["compact_256m_us"] = round(c_ms * 1e3, 1)
+        # its ceiling: the same tile and grid reading every key and writing half of them, no scan
+        cvpt = int(L.ds_tile_elems(ds.DS_UINT32, ds._binding.TILE_OF["compact"])) * 4 // 4096
+        h_ms = timed(lambda: L.ds_bandwidth_pattern(3, cvpt, 0, keys.data_ptr(), kout.data_ptr(), nk * 4, sh), reps=10)
+        extras["compact_ceiling_256m_us"] = round(h_ms * 1e3, 1)
+        extras["compact_over_ceiling"] = round(h_ms / c_ms, 4)
         extras["compact_256m_gelem_s"] = round(nk / (c_ms * 1e-3) / 1e9, 2)
         extras["compact_256m_alg_gbs"] = round(cbytes / (c_ms * 1e-3) / 1e9, 1)
         # the order-free form: atomic space claims per wave (the pages') and per workgroup
@@ -551,10 +712,17 @@ def main():
                    "tile_elems": {"int32": int(L.ds_tile_elems(ds.DS_INT32, 0)),
                                   "fp32": int(L.ds_tile_elems(ds.DS_FP32, 0))},
                    "workgroup": 256},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (cold_ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 /
+                                                                          PEAK_HBM_GBS, 4),
+                     "frac_basis": "cold: median launch time of 50 int32 and 50 fp32 launches, each after a 1 GiB "
+                                   "read evicting L2 and the memory-side cache (HIP events on the launch stream)",
+                     "launch_us_cold_median": round(cold_ms * 1e3, 2),
+                     "achieved_warm": round(achieved, 1), "frac_warm": round(achieved / PEAK_HBM_GBS, 4),
+                     "warm_basis": f"mean launch time over the {K} timed back-to-back steps",
+                     "launch_us_mean": round(launch_ms * 1e3, 2),
                      "traffic": traffic, "kernel": "lookback_scan_kernel",
-                     "alg_bytes_per_launch": int(alg_bytes), "launch_us_mean": round(launch_ms * 1e3, 2)},
+                     "alg_bytes_per_launch": int(alg_bytes)},
         "cpu_baseline": cpu,
         "extras": extras,
     }

@@ -235,6 +235,31 @@ int ds_moe_align(const int32_t* d_topk_ids, int64_t n, int num_experts, int bloc
  */
 int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream);
 
+/* Access pattern of ds_bandwidth_pattern. */
+typedef enum {
+    DS_PATTERN_READ = 0,       /* read nbytes (folded on chip; nothing written) */
+    DS_PATTERN_WRITE = 1,      /* write nbytes (d_in unused, may be NULL) */
+    DS_PATTERN_COPY = 2,       /* read then write each tile: the held tile of the look-back scan */
+    DS_PATTERN_READ_HALF = 3   /* read each tile, write its first half contiguously: compaction's bytes
+                                  at half kept, with no scan */
+} ds_pattern;
+
+/*
+ * Bandwidth probe for the ceiling table the scan and the compaction are read
+ * against (the "copy, no scan" row of "Day 32 -- The CUDA scan algorithm",
+ * section "Results", widened to reads, writes and tile sizes): 256-thread
+ * workgroups each move vectors_per_thread (1, 2, 4, 8, 16 or 28) 16-byte
+ * vectors per thread with non-temporal accesses. layout 0: each workgroup a
+ * contiguous tile, laid out as the scan's (lane l of wave w holds vectors
+ * k * 64 + l of the wave's quarter); layout 1: 4 KiB chunks at a 32 KiB
+ * stride (8 consecutive workgroups share 8 * vectors_per_thread chunks, the
+ * g-th taking every 8th from chunk g % 8). nbytes a multiple of 16, pointers
+ * 16-byte aligned, in and out not overlapping. Returns DS_OK or a ds_status
+ * error.
+ */
+int ds_bandwidth_pattern(int mode, int vectors_per_thread, int layout, const void* d_in, void* d_out, int64_t nbytes,
+                         hipStream_t stream);
+
 /*
  * The pages' block-scan experiment on gfx950: each 4,096-element tile of d_in
  * is scanned (exclusive) by one 1,024-thread workgroup in LDS with the given

@@ -30,12 +30,13 @@ DS_ERR_TOO_LARGE = 7
 DS_ERR_STREAM_CAPTURING = 8
 
 EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "ds_scan_seeded", "compact_if", "ds_compact_unordered", "ds_radix_pass",
-           "ds_moe_align", "ds_copy", "ds_tile_scan", "ds_tile_pipeline",
+           "ds_moe_align", "ds_copy", "ds_bandwidth_pattern", "ds_tile_scan", "ds_tile_pipeline",
            "ds_tile_elems", "ds_scan_tile_elems", "ds_query_timeout", "ds_fail_next_allocations", "ds_set_spin_limit",
            "ds_status_string", "ds_release_workspace", "ds_version"]
 TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4,
            "counting_sort": 5, "counting_sort_values": 6, "moe_align": 7}
 TILE_VARIANTS = {"tree": 0, "tree_pad1": 1, "tree_pad2": 2, "hillis_steele": 3}
+PATTERNS = {"read": 0, "write": 1, "copy": 2, "read_half": 3}
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -61,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ds_moe_align.restype = I
     L.ds_copy.argtypes = [P, P, I64, P]
     L.ds_copy.restype = I
+    L.ds_bandwidth_pattern.argtypes = [I, I, I, P, P, I64, P]
+    L.ds_bandwidth_pattern.restype = I
     L.ds_tile_scan.argtypes = [I, I, P, P, P, I64, P]
     L.ds_tile_scan.restype = I
     L.ds_tile_pipeline.argtypes = [I, I, P, P, I64, P]

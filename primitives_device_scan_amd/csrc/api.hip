@@ -328,6 +328,24 @@ int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream)
     return ds::launch_copy(d_in, d_out, nbytes, stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
+int ds_bandwidth_pattern(int mode, int vectors_per_thread, int layout, const void* d_in, void* d_out, int64_t nbytes,
+                         hipStream_t stream)
+{
+    if (mode < 0 || mode > 3 || layout < 0 || layout > 1 || !ds::pattern_vpt_ok(vectors_per_thread))
+        return DS_ERR_INVALID_VALUE;
+    if (nbytes < 0 || (nbytes % 16)) return DS_ERR_INVALID_VALUE;
+    if (nbytes == 0) return DS_OK;
+    if (!d_out || (mode != 1 && !d_in)) return DS_ERR_INVALID_VALUE;
+    if (((uintptr_t)d_in % 16) || ((uintptr_t)d_out % 16)) return DS_ERR_MISALIGNED;
+    if (mode != 1) {
+        const uintptr_t a = (uintptr_t)d_in, b = (uintptr_t)d_out, len = (uintptr_t)nbytes;
+        if (a < b + len && b < a + len) return DS_ERR_OVERLAP;
+    }
+    if (nbytes / 4096 + 8 >= kMaxTiles) return DS_ERR_TOO_LARGE;
+    return ds::launch_pattern(mode, vectors_per_thread, layout, d_in, d_out, nbytes, stream) == hipSuccess ? DS_OK
+                                                                                                        : DS_ERR_HIP;
+}
+
 static int check_tile_args(int dtype, int variant, const void* in, void* out, int64_t n)
 {
     if (!valid_dtype(dtype)) return DS_ERR_UNSUPPORTED_DTYPE;

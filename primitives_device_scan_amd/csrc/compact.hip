@@ -55,6 +55,8 @@ __global__ __launch_bounds__(kThreads, kCompactOcc) void compact_kernel(const T*
     const int wave = (int)(threadIdx.x / kWave);
     const int64_t tile = blockIdx.x;
     const uint32_t epoch = (num_tiles > 1 && wave == 0) ? launch_epoch(ctrl) : 0u;
+    uint64_t touched = 0;
+    if (num_tiles > 1 && threadIdx.x == 0) touched = touch_status(status, tile);
 
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
     const bool whole = seg + S::kWaveElems <= n;
@@ -133,6 +135,7 @@ __global__ __launch_bounds__(kThreads, kCompactOcc) void compact_kernel(const T*
                                                                        __HIP_MEMORY_SCOPE_AGENT) != 0u);
         *num_selected = bad ? (int64_t)-1 : (int64_t)prefix + agg;
     }
+    if (threadIdx.x == 0) keep_alive(touched);
 }
 
 __global__ void write_count_kernel(int64_t* p, int64_t v) { *p = v; }

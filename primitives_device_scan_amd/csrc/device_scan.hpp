@@ -11,23 +11,19 @@ namespace ds {
 // 16-byte vectors per thread (VPT); a tile is 256 threads x VPT x 16 B.
 //  - look-back scan: large tiles, since resident tile bytes per CU are what
 //    hide the look-back latency (several microseconds under full HBM load)
-//    behind other tiles' transfers: 112 KiB for 4-byte types (fp32 inclusive
-//    104 KiB, the largest that does not spill) at 3 workgroups per CU, 144 / 112 KiB for 8-byte types
-//    (exclusive / inclusive) at 2 per CU (ScanOcc). Measured at n = 100M:
-//    against 96 KiB tiles at 4 per CU, the 4-byte scans 1.5-2.5% faster in all
-//    four cases, though the int32 tiles spill 12 bytes per thread (as the 96
-//    KiB int32 tile did 24 at 4 per CU), while 120-128 KiB tiles or 2 per CU
-//    were slower; against 80 / 64 KiB at 3 per CU, int64 5-6% (exclusive) and
-//    7% (inclusive) faster (144 KiB exclusive tiles 1-1.4% faster than 128);
-//    8-byte tiles of 96-112 KiB at 3 per CU spill 70-430 bytes and are
-//    slower, and 160 KiB at 2 per CU too;
+//    behind other tiles' transfers. 4-byte types: 80 KiB tiles (20 vectors
+//    per thread, 131-145 VGPRs, no spill) at 3 workgroups per CU. Measured on
+//    MI355X at n = 100M with the status words padded to a line each, 80-96 KiB
+//    tiles at 3 per CU take 138-141 us warm or after a cache eviction alike;
+//    112 KiB tiles (28 vectors) spill 28-40 bytes per lane and lose 5-8 us
+//    after an eviction, 64-76 KiB tiles (3 or 4 per CU) are 1-3 us slower.
+//    8-byte types: 144 / 112 KiB tiles (exclusive / inclusive) at 2 per CU
+//    (ScanOcc); 96-112 KiB at 3 per CU spill and were slower, 128 KiB 1% slower;
 //  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
 //    wait to hide; compaction's keep mask holds 64 elements).
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
-    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 36)
-                               : __is_same(T, float) ? (INCLUSIVE ? 26 : 28)
-                                                     : 28;
+    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 36) : 20;
 };
 // Workgroups per CU the look-back kernel is compiled for (waves per SIMD):
 // the large 8-byte tiles need up to 256 VGPRs; every other tile fits 3.
@@ -35,7 +31,7 @@ template <typename T, int VPT>
 struct ScanOcc {
     static constexpr int value = (sizeof(T) == 8 && VPT > 20) ? 2 : 3;
 };
-constexpr int kVPT = 28;  // largest scan tile: the same-pattern copy uses it
+constexpr int kVPT = 20;  // the 4-byte scan tile: the same-pattern copy (ds_copy) uses it
 constexpr int kThreePassVPT = 16;
 constexpr int kCompactVPT = 16;
 constexpr int kCompactOcc = 4;  // workgroups per CU the ordered compaction is compiled for
@@ -70,6 +66,19 @@ __device__ __forceinline__ uint32_t launch_epoch(Ctrl* ctrl)
 {
     return __hip_atomic_load(&ctrl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Read of the tile's own status line as the tile starts, long before the
+// tile publishes into it: the line is then fetched while the tile's data
+// loads, and the publish and its successors' polls find it nearby. Measured
+// at n = 100M (int32 exclusive, 112 KiB tiles) the whole scan is 1-2% faster,
+// most after a cache eviction. The value is unused; keep_alive() consumes it
+// at the end of the kernel so the load is not dropped.
+__device__ __forceinline__ uint64_t touch_status(uint64_t* status, int64_t tile)
+{
+    return status_load(status + tile * kStatusWords);
+}
+
+__device__ __forceinline__ void keep_alive(uint64_t v) { asm volatile("" ::"v"(v)); }
 
 // Called by one thread as soon as the tile aggregate is known: tile 0
 // publishes its inclusive prefix `first + agg` (first: 0, or the seed of a

@@ -23,6 +23,8 @@ __global__ __launch_bounds__(kThreads, (ScanOcc<T, VPT>::value)) void lookback_s
     const int64_t tile = blockIdx.x;
     // Only wave 0 publishes and looks back; its epoch load overlaps the data loads.
     const uint32_t epoch = (num_tiles > 1 && wave == 0) ? launch_epoch(ctrl) : 0u;
+    uint64_t touched = 0;
+    if (num_tiles > 1 && threadIdx.x == 0) touched = touch_status(status, tile);
 
     const int64_t seg = tile * S::kTile + (int64_t)wave * S::kWaveElems;
     // Whole waves take 16-byte vectors whatever the alignment (A16: in and out
@@ -53,6 +55,7 @@ __global__ __launch_bounds__(kThreads, (ScanOcc<T, VPT>::value)) void lookback_s
         store_vec<T, VPT, A16>(out, seg, lane, e);
     else
         store_scalar<T, VPT>(out, seg, n, lane, e);
+    if (threadIdx.x == 0) keep_alive(touched);
 }
 
 // Vectors per thread for n elements: the per-type large tile (ScanVPT) from

@@ -190,6 +190,19 @@ def test_copy_validation(lib):
     assert lib.ds_copy(A, A + 16, 64, None) == OVL
 
 
+def test_bandwidth_pattern_validation(lib):
+    f = lib.ds_bandwidth_pattern
+    assert f(4, 1, 0, A, B, 4096, None) == INV       # bad mode
+    assert f(0, 3, 0, A, B, 4096, None) == INV       # vectors per thread not offered
+    assert f(0, 1, 2, A, B, 4096, None) == INV       # bad layout
+    assert f(0, 1, 0, A, B, 4100, None) == INV       # not whole vectors
+    assert f(0, 1, 0, A, B, 0, None) == OK           # nothing to do
+    assert f(0, 1, 0, None, B, 4096, None) == INV
+    assert f(0, 1, 0, A + 4, B, 4096, None) == MIS
+    assert f(2, 4, 1, A, A + 16, 4096, None) == OVL
+    assert f(1, 4, 1, None, B, 1 << 50, None) == BIG  # write only: no input needed
+
+
 def test_tile_queries(lib):
     from primitives_device_scan_amd import _binding
     # host-only queries: every tile is whole waves of a 256-thread workgroup;
