@@ -229,7 +229,7 @@ def tile_lds_experiment(args):
 def ceiling_experiment(args):
     """The access-pattern table the scan and the compaction are read against:
     ds_bandwidth_pattern for read / write / copy / read-all-write-half at 4,
-    16, 64 and 112 KiB per workgroup, contiguous tiles (the scan's layout) and
+    16, 64, 80 and 112 KiB per workgroup, contiguous tiles (the scan's layout) and
     4 KiB chunks at a 32 KiB stride, on 400,000,016 bytes per buffer (the
     100M-element scan's input); plus ds_copy (the scan's own tile) and
     compact_if's read-all-write-half pattern at its 64 KiB tile on 1 GiB.
@@ -265,7 +265,7 @@ def ceiling_experiment(args):
     rows = []
     for mode, mcode in ds._binding.PATTERNS.items():
         moved = {"read": 1.0, "write": 1.0, "copy": 2.0, "read_half": 1.5}[mode]
-        for vpt in (1, 4, 16, 28):
+        for vpt in (1, 4, 16, 20, 28):
             for layout in (0, 1):
                 def fn():
                     st = L.ds_bandwidth_pattern(mcode, vpt, layout, a.data_ptr(), b.data_ptr(), nbytes, sh)

@@ -248,7 +248,7 @@ typedef enum {
  * Bandwidth probe for the ceiling table the scan and the compaction are read
  * against (the "copy, no scan" row of "Day 32 -- The CUDA scan algorithm",
  * section "Results", widened to reads, writes and tile sizes): 256-thread
- * workgroups each move vectors_per_thread (1, 2, 4, 8, 16 or 28) 16-byte
+ * workgroups each move vectors_per_thread (1, 2, 4, 8, 16, 20 or 28) 16-byte
  * vectors per thread with non-temporal accesses. layout 0: each workgroup a
  * contiguous tile, laid out as the scan's (lane l of wave w holds vectors
  * k * 64 + l of the wave's quarter); layout 1: 4 KiB chunks at a 32 KiB

@@ -141,12 +141,16 @@ static hipError_t pattern_mode(int vpt, int layout, const void* in, void* out, i
     case 4: return pattern_launch<MODE, 4>(layout, in, out, nvec, st);
     case 8: return pattern_launch<MODE, 8>(layout, in, out, nvec, st);
     case 16: return pattern_launch<MODE, 16>(layout, in, out, nvec, st);
+    case 20: return pattern_launch<MODE, 20>(layout, in, out, nvec, st);
     case 28: return pattern_launch<MODE, 28>(layout, in, out, nvec, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-bool pattern_vpt_ok(int vpt) { return vpt == 1 || vpt == 2 || vpt == 4 || vpt == 8 || vpt == 16 || vpt == 28; }
+bool pattern_vpt_ok(int vpt)
+{
+    return vpt == 1 || vpt == 2 || vpt == 4 || vpt == 8 || vpt == 16 || vpt == 20 || vpt == 28;
+}
 
 hipError_t launch_pattern(int mode, int vpt, int layout, const void* in, void* out, int64_t nbytes,
                           hipStream_t stream)

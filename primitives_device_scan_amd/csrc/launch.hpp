@@ -45,7 +45,7 @@ hipError_t launch_compact_unordered(ElemKind kind, const void* in, void* out, in
 hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t stream);
 
 // Access-pattern probes (ds_bandwidth_pattern): mode 0 read, 1 write, 2 copy,
-// 3 read all / write half; vpt 1, 2, 4, 8, 16 or 28; layout 0 contiguous,
+// 3 read all / write half; vpt 1, 2, 4, 8, 16, 20 or 28; layout 0 contiguous,
 // 1 4 KiB chunks at a 32 KiB stride.
 bool pattern_vpt_ok(int vpt);
 hipError_t launch_pattern(int mode, int vpt, int layout, const void* in, void* out, int64_t nbytes,
