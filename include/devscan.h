@@ -148,6 +148,22 @@ int ds_scan_seeded(int dtype, int inclusive, const void* d_in, void* d_out, int6
                    hipStream_t stream);
 
 /*
+ * The look-back scan (as ds_scan with DS_ALGO_LOOKBACK, `inclusive` 0 or 1)
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It calls no
+ * allocating routine: its control block and status words live in a fixed
+ * 4 MiB array in the library's own device memory, one per GPU, held until the
+ * process ends, with room for 32,766 tiles (n up to about 670M 4-byte or
+ * 469M 8-byte elements; DS_ERR_TOO_LARGE beyond). Every call on a GPU shares
+ * that GPU's array, so calls that overlap in time on one GPU (different
+ * streams, no ordering between them) race and give wrong results; order them
+ * on one stream. The first call on a device enqueues a kernel that clears
+ * the array. ds_query_timeout reports a give-up of these calls too (once
+ * they have finished). Other arguments and errors as scan_exclusive.
+ */
+int ds_scan_noalloc(int dtype, int inclusive, const void* d_in, void* d_out, int64_t n, hipStream_t stream);
+
+/*
  * Order-preserving stream compaction: writes, in input order, every d_in[i]
  * with (d_in[i] CMP operand) to d_out[0 .. k) and k to *d_num_selected (one
  * int64 in device memory; -1 if the last tile saw a look-back wait give up). "Prefix sum and other parallel patterns", section

@@ -29,7 +29,7 @@ DS_ERR_MISALIGNED = 6
 DS_ERR_TOO_LARGE = 7
 DS_ERR_STREAM_CAPTURING = 8
 
-EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "ds_scan_seeded", "compact_if", "ds_compact_unordered", "ds_radix_pass",
+EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "ds_scan_seeded", "ds_scan_noalloc", "compact_if", "ds_compact_unordered", "ds_radix_pass",
            "ds_moe_align", "ds_copy", "ds_bandwidth_pattern", "ds_tile_scan", "ds_tile_pipeline",
            "ds_tile_elems", "ds_scan_tile_elems", "ds_query_timeout", "ds_fail_next_allocations", "ds_set_spin_limit",
            "ds_status_string", "ds_release_workspace", "ds_version"]
@@ -52,6 +52,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ds_scan.restype = I
     L.ds_scan_seeded.argtypes = [I, I, P, P, I64, P, P]
     L.ds_scan_seeded.restype = I
+    L.ds_scan_noalloc.argtypes = [I, I, P, P, I64, P]
+    L.ds_scan_noalloc.restype = I
     L.compact_if.argtypes = [I, P, P, P, I64, I, ctypes.c_uint64, P]
     L.compact_if.restype = I
     L.ds_compact_unordered.argtypes = [I, P, P, P, I64, I, ctypes.c_uint64, I, P]

@@ -12,6 +12,16 @@
 #include "launch.hpp"
 #include "tile.hpp"
 
+// Scratch of ds_scan_noalloc (see below); 256-byte aligned like a HIP allocation.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+__global__ void noalloc_clear_kernel(uint64_t* p, int64_t words)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
 namespace {
 
 using ds::Ctrl;
@@ -150,6 +160,23 @@ int get_aux(hipStream_t stream, size_t bytes, char** out)
     return DS_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free look-back scan (ds_scan_noalloc): its control block and
+// status words live in `scratch`, a fixed array in the library's own device
+// memory, one copy per GPU, held until the process ends. Host code never
+// passes `scratch` itself to a kernel (in host code the name is a host-side
+// stand-in); it takes each device's address once with hipGetSymbolAddress and
+// uses that.
+// ---------------------------------------------------------------------------
+constexpr int64_t kNoAllocMaxTiles = (int64_t)((kNoAllocScratchBytes - sizeof(Ctrl)) / kStatusBytes);
+
+struct NoAllocDev {
+    char* ptr = nullptr;           // device address of this GPU's `scratch`
+    bool cleared = false;          // the clear kernel has been enqueued once
+    uint64_t launches = 0;         // launches since the last clear (epoch wrap guard)
+};
+std::map<int, NoAllocDev> g_noalloc;  // per device, guarded by g_mu
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -267,6 +294,49 @@ int ds_scan_seeded(int dtype, int inclusive, const void* d_in, void* d_out, int6
         if (overlaps(d_seed, (size_t)sz, d_out, (size_t)(n * sz))) return DS_ERR_OVERLAP;
     }
     return scan_impl(dtype, inclusive, DS_ALGO_LOOKBACK, d_in, d_out, n, stream, d_seed);
+}
+
+int ds_scan_noalloc(int dtype, int inclusive, const void* d_in, void* d_out, int64_t n, hipStream_t stream)
+{
+    if (inclusive != 0 && inclusive != 1) return DS_ERR_INVALID_VALUE;
+    int st = check_io(dtype, d_in, d_out, n, true);
+    if (st != DS_OK || n == 0) return st;
+    const int64_t te = ds::tile_elems(kind_of(dtype), inclusive != 0, n);
+    const int64_t tiles = (n + te - 1) / te;
+    if (tiles > kNoAllocMaxTiles) return DS_ERR_TOO_LARGE;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
+    NoAllocDev& d = g_noalloc[dev];
+    if (!d.ptr) {
+        // Once per device, with that device current: this GPU's copy of the array.
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return DS_ERR_HIP;
+        }
+        d.ptr = static_cast<char*>(p);
+    }
+    DevWs dws{nullptr, nullptr, nullptr};
+    if (tiles > 1) {
+        if (!d.cleared || d.launches >= kEpochClearPeriod) {
+            // Zero the control block and every status word (a kernel, so that
+            // a captured call records no memset node); stream-ordered before
+            // the scan below.
+            const int64_t words = (int64_t)(kNoAllocScratchBytes / sizeof(uint64_t));
+            noalloc_clear_kernel<<<dim3(256), dim3(256), 0, stream>>>(reinterpret_cast<uint64_t*>(d.ptr), words);
+            if (hipGetLastError() != hipSuccess) return DS_ERR_HIP;
+            d.cleared = true;
+            d.launches = 0;
+        }
+        dws.ctrl = reinterpret_cast<Ctrl*>(d.ptr);
+        dws.status = reinterpret_cast<uint64_t*>(d.ptr + sizeof(Ctrl));
+    }
+    const hipError_t e =
+        ds::launch_lookback_scan(kind_of(dtype), inclusive != 0, d_in, d_out, n, dws, g_spin_limit, stream);
+    if (e != hipSuccess) return DS_ERR_HIP;
+    if (tiles > 1) ++d.launches;
+    return DS_OK;
 }
 
 int compact_if(int dtype, const void* d_in, void* d_out, int64_t* d_num_selected, int64_t n, int cmp,
@@ -388,8 +458,23 @@ int ds_query_timeout(hipStream_t stream, int* timed_out)
     std::lock_guard<std::mutex> lock(g_mu);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
+    int from_scratch = 0;
+    auto na = g_noalloc.find(dev);
+    if (na != g_noalloc.end() && na->second.ptr && na->second.cleared) {
+        // ds_scan_noalloc's flag: the same rule, on the device's scratch array
+        Ctrl* c = reinterpret_cast<Ctrl*>(na->second.ptr);
+        uint32_t flag = 0;
+        if (hipMemcpy(&flag, &c->timeout, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return DS_ERR_HIP;
+        if (flag) {
+            na->second.cleared = false;  // the next ds_scan_noalloc clears every word first
+            from_scratch = 1;
+        }
+    }
     auto it = g_ws.find({dev, stream});
-    if (it == g_ws.end() || !it->second.base) return DS_OK;
+    if (it == g_ws.end() || !it->second.base) {
+        *timed_out = from_scratch;
+        return DS_OK;
+    }
     Workspace& w = it->second;
     Ctrl* c = reinterpret_cast<Ctrl*>(w.base);
     uint32_t flag = 0;
@@ -404,7 +489,7 @@ int ds_query_timeout(hipStream_t stream, int* timed_out)
         if (hipMemcpy(&c->timeout, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return DS_ERR_HIP;
         w.lookback_launches = 0;
     }
-    *timed_out = flag ? 1 : 0;
+    *timed_out = (flag || from_scratch) ? 1 : 0;
     return DS_OK;
 }
 

@@ -70,6 +70,20 @@ def test_status_values_match_the_header():
         "DS_ERR_HIP", "DS_ERR_MISALIGNED", "DS_ERR_TOO_LARGE", "DS_ERR_STREAM_CAPTURING")]
 
 
+def test_scan_noalloc_validation(lib):
+    f = lib.ds_scan_noalloc
+    assert f(7, 0, A, B, 10, None) == DTY
+    assert f(0, 2, A, B, 10, None) == INV         # inclusive not 0/1
+    assert f(0, 0, A, B, -1, None) == INV
+    assert f(0, 0, None, B, 10, None) == INV
+    assert f(0, 0, None, None, 0, None) == OK     # n == 0: nothing to do
+    assert f(0, 0, A + 2, B, 10, None) == MIS
+    assert f(0, 0, A, A + 4, 10, None) == OVL
+    far = A + (16 << 30)                           # no overlap with A at these sizes
+    assert f(0, 0, A, far, 1_000_000_000, None) == BIG   # more tiles than the fixed scratch holds
+    assert f(3, 1, A, far, 600_000_000, None) == BIG
+
+
 def test_fail_next_allocations_arguments(lib):
     assert lib.ds_fail_next_allocations(-1) == INV
     assert lib.ds_fail_next_allocations(0) == OK
