@@ -348,6 +348,8 @@ def main():
                     help="the access-pattern ceiling table instead of the main bench (own JSON line)")
     ap.add_argument("--cold", action="store_true",
                     help="with --profile-only: a 1 GiB read before every scan launch (the cold protocol)")
+    ap.add_argument("--algo", default="default",
+                    help="with --profile-only: the ds_scan algorithm the scans use (default, lookback_blocked, ...)")
     ap.add_argument("--pattern", default=None,
                     help="with --profile-only: MODE:VPT:LAYOUT of ds_bandwidth_pattern to launch --steps times "
                          "instead of the scans (e.g. write:28:0)")
@@ -388,13 +390,15 @@ def main():
     d_yf = torch.empty_like(d_xf)
     torch.cuda.synchronize()
 
+    algo = ds.ALGO[args.algo] if args.profile_only else 0  # the timed bench always runs the library default
+
     def scan_i():
-        st = L.scan_exclusive(ds.DS_INT32, d_xi.data_ptr(), d_yi.data_ptr(), n, sh)
+        st = L.ds_scan(ds.DS_INT32, 0, algo, d_xi.data_ptr(), d_yi.data_ptr(), n, sh)
         if st:
             raise ds.DevscanError(st, "scan_exclusive int32")
 
     def scan_f():
-        st = L.scan_exclusive(ds.DS_FP32, d_xf.data_ptr(), d_yf.data_ptr(), n, sh)
+        st = L.ds_scan(ds.DS_FP32, 0, algo, d_xf.data_ptr(), d_yf.data_ptr(), n, sh)
         if st:
             raise ds.DevscanError(st, "scan_exclusive fp32")
 
@@ -507,6 +511,12 @@ def main():
     tp_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 0, ds.ALGO["three_pass"], d_xi.data_ptr(), d_yi.data_ptr(), n, sh))
     extras["three_pass_int32_gelem_s"] = round(n / (tp_ms * 1e-3) / 1e9, 2)
     extras["three_pass_int32_alg_gbs"] = round(alg_bytes / (tp_ms * 1e-3) / 1e9, 1)
+    # the blocked tile layout (a measured alternative): both scans, warm and cold
+    for name, dcode, dx, dy in (("int32", ds.DS_INT32, d_xi, d_yi), ("fp32", ds.DS_FP32, d_xf, d_yf)):
+        bf = lambda: L.ds_scan(dcode, 0, ds.ALGO["lookback_blocked"], dx.data_ptr(), dy.data_ptr(), n, sh)
+        extras[f"{name}_excl_blocked_us"] = round(timed(bf) * 1e3, 2)
+        extras[f"{name}_excl_blocked_cold_us_median"] = round(
+            float(np.median(cold_times_ms(torch, stream, bf, evict, reps=20))) * 1e3, 2)
     # inclusive at the headline size, reusing its buffers
     ii_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 1, 0, d_xi.data_ptr(), d_yi.data_ptr(), n, sh))
     extras["int32_incl_100m_us"] = round(ii_ms * 1e3, 1)

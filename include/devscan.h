@@ -67,7 +67,10 @@ typedef enum { DS_LT = 0, DS_LE = 1, DS_GT = 2, DS_GE = 3, DS_EQ = 4, DS_NE = 5 
 typedef enum {
     DS_ALGO_DEFAULT = 0,   /* the single-pass look-back scan */
     DS_ALGO_LOOKBACK = 1,  /* one launch: tiles publish aggregates / inclusive prefixes and look back */
-    DS_ALGO_THREE_PASS = 2 /* three launches: reduce tiles, scan tile totals, rescan tiles seeded */
+    DS_ALGO_THREE_PASS = 2, /* three launches: reduce tiles, scan tile totals, rescan tiles seeded */
+    DS_ALGO_LOOKBACK_BLOCKED = 3 /* the look-back scan with each tile transposed through LDS so that a
+                                    thread scans contiguous elements (4-byte types only; a measured
+                                    alternative to the default striped tile) */
 } ds_algo;
 
 /* Block-level tile scan held in LDS, for ds_tile_scan / ds_tile_pipeline. */
@@ -123,6 +126,7 @@ int scan_inclusive(int dtype, const void* d_in, void* d_out, int64_t n, hipStrea
  * (section "One block scans 4,096. Ten million needs three kernels.") in its
  * reduce-then-scan form: pass 1 only reads (tile totals), pass 2 scans the
  * totals in one workgroup, pass 3 rescans each tile seeded with its offset.
+ * DS_ALGO_LOOKBACK_BLOCKED returns DS_ERR_UNSUPPORTED_DTYPE for 8-byte types.
  * Other arguments and errors as scan_exclusive.
  */
 int ds_scan(int dtype, int inclusive, int algo, const void* d_in, void* d_out, int64_t n,

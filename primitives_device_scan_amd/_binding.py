@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdevscan.
 # ds_dtype, ds_cmp, ds_algo, ds_status (include/devscan.h)
 DS_INT32, DS_UINT32, DS_FP32, DS_INT64, DS_UINT64 = range(5)
 CMP = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
-ALGO = {"default": 0, "lookback": 1, "three_pass": 2}
+ALGO = {"default": 0, "lookback": 1, "three_pass": 2, "lookback_blocked": 3}
 DS_OK = 0
 DS_ERR_INVALID_VALUE = 1
 DS_ERR_UNSUPPORTED_DTYPE = 2

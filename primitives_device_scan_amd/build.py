@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdevscan.so")
-SOURCES = ["scan_lookback.hip", "scan_three_pass.hip", "compact.hip", "compact_unordered.hip", "counting_sort.hip", "copy.hip", "tile_lds.hip", "api.hip"]
+SOURCES = ["scan_lookback.hip", "scan_blocked.hip", "scan_three_pass.hip", "compact.hip", "compact_unordered.hip", "counting_sort.hip", "copy.hip", "tile_lds.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -235,9 +235,26 @@ int scan_impl(int dtype, int inclusive, int algo, const void* in, void* out, int
               const void* seed = nullptr)
 {
     if (inclusive != 0 && inclusive != 1) return DS_ERR_INVALID_VALUE;
-    if (algo < DS_ALGO_DEFAULT || algo > DS_ALGO_THREE_PASS) return DS_ERR_INVALID_VALUE;
+    if (algo < DS_ALGO_DEFAULT || algo > DS_ALGO_LOOKBACK_BLOCKED) return DS_ERR_INVALID_VALUE;
     int st = check_io(dtype, in, out, n, true);
     if (st != DS_OK || n == 0) return st;
+    if (algo == DS_ALGO_LOOKBACK_BLOCKED) {
+        if (elem_bytes(dtype) != 4) return DS_ERR_UNSUPPORTED_DTYPE;
+        const int64_t bt = ds::blocked_tile_elems(n);
+        const int64_t btiles = (n + bt - 1) / bt;
+        std::lock_guard<std::mutex> lock(g_mu);
+        DevWs dws{nullptr, nullptr, nullptr};
+        Workspace* w = nullptr;
+        if (btiles > 1) {
+            st = get_workspace(stream, btiles, &w);
+            if (st != DS_OK) return st;
+            dws = view(*w);
+        }
+        const hipError_t e =
+            ds::launch_lookback_blocked(kind_of(dtype), inclusive != 0, in, out, n, dws, g_spin_limit, stream);
+        if (w && e == hipSuccess) ++w->lookback_launches;
+        return e == hipSuccess ? DS_OK : DS_ERR_HIP;
+    }
     // Choose the kernel first, then size the workspace by that kernel's own
     // tiles: the look-back and three-pass tiles differ in size, and a
     // three-pass call on one tile runs the look-back kernel instead.

@@ -29,6 +29,12 @@ hipError_t launch_lookback_scan(ElemKind kind, bool inclusive, const void* in, v
                                 const DevWs& ws, uint32_t spin_limit, hipStream_t stream,
                                 const void* seed = nullptr);
 
+// The look-back scan with the tile transposed through LDS (blocked layout;
+// 4-byte types only) and its tile for n elements.
+hipError_t launch_lookback_blocked(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
+                                   const DevWs& ws, uint32_t spin_limit, hipStream_t stream);
+int64_t blocked_tile_elems(int64_t n);
+
 hipError_t launch_three_pass_scan(ElemKind kind, bool inclusive, const void* in, void* out, int64_t n,
                                   const DevWs& ws, hipStream_t stream);
 

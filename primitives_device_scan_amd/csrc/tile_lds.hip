@@ -39,11 +39,39 @@ constexpr int padded_words()
     return PAD == 0 ? kLdsTile : PAD == 1 ? kLdsTile + kLdsTile / 32 : kLdsTile + kLdsTile / 32 + kLdsTile / 1024;
 }
 
-// Work-efficient tree. Level `stride` of the up-sweep adds word
-// (2a+1)*stride-1 into word (2a+2)*stride-1 for a = 0 .. 4096/(2*stride)-1;
-// the down-sweep visits the same pairs from the top, handing each right word's
-// value to the left word and the sum of both to the right word. Every thread
-// reaches every barrier, active or not.
+// Work-efficient tree over the 4,096 words of a tile, written by tree level
+// lv = 0 .. 11. At level lv the words fall into blocks of 2^(lv+1); block a
+// owns two nodes, the last word of its first half (its left node) and its
+// last word (its right node), and one thread handles one block. Going up, the
+// right node accumulates the left one, so each right node ends up holding the
+// sum of its block. The root (word 4,095) then holds the tile total; the tile
+// keeps that total and sets the root to 0, the exclusive prefix of the tile.
+// Coming down, each block's right node holds the sum of everything before the
+// block: the left node takes that value, and the right node adds the first
+// half's sum to it. Every thread reaches every barrier, active or not.
+constexpr int kLdsLevels = 12;  // 2^12 = kLdsTile
+
+__device__ __forceinline__ int left_node(int a, int lv) { return (a << (lv + 1)) | ((1 << lv) - 1); }
+__device__ __forceinline__ int right_node(int a, int lv) { return (a << (lv + 1)) | ((2 << lv) - 1); }
+
+template <typename T, int PAD, bool UP>
+__device__ __forceinline__ void tree_level(T* tile, int lv)
+{
+    const int blocks = kLdsTile >> (lv + 1);
+    for (int a = (int)threadIdx.x; a < blocks; a += kLdsThreads) {
+        const int l = padded<PAD>(left_node(a, lv)), r = padded<PAD>(right_node(a, lv));
+        const T first_half = tile[l];
+        const T node = tile[r];
+        if constexpr (UP) {
+            tile[r] = node + first_half;
+        } else {
+            tile[l] = node;               // everything before the block
+            tile[r] = node + first_half;  // ... and its first half
+        }
+    }
+    __syncthreads();
+}
+
 template <typename T, int PAD>
 __global__ __launch_bounds__(kLdsThreads) void tree_tile_kernel(const T* in, T* out, T* tile_sums, int64_t n)
 {
@@ -56,31 +84,14 @@ __global__ __launch_bounds__(kLdsThreads) void tree_tile_kernel(const T* in, T* 
         tile[padded<PAD>(i)] = base + i < n ? in[base + i] : T(0);
     }
     __syncthreads();
-    for (int stride = 1; stride < kLdsTile; stride <<= 1) {
-        const int pairs = kLdsTile / (2 * stride);
-        for (int a = tid; a < pairs; a += kLdsThreads) {
-            const int lo = (2 * a + 1) * stride - 1, hi = (2 * a + 2) * stride - 1;
-            tile[padded<PAD>(hi)] = tile[padded<PAD>(hi)] + tile[padded<PAD>(lo)];
-        }
-        __syncthreads();
-    }
+    for (int lv = 0; lv < kLdsLevels; ++lv) tree_level<T, PAD, true>(tile, lv);
     if (tid == 0) {
-        // The total leaves before the root is cleared; the cleared root seeds the down-sweep.
-        if (tile_sums) tile_sums[blockIdx.x] = tile[padded<PAD>(kLdsTile - 1)];
-        tile[padded<PAD>(kLdsTile - 1)] = T(0);
+        T& root = tile[padded<PAD>(kLdsTile - 1)];
+        if (tile_sums) tile_sums[blockIdx.x] = root;
+        root = T(0);
     }
     __syncthreads();
-    for (int stride = kLdsTile / 2; stride >= 1; stride >>= 1) {
-        const int pairs = kLdsTile / (2 * stride);
-        for (int a = tid; a < pairs; a += kLdsThreads) {
-            const int lo = (2 * a + 1) * stride - 1, hi = (2 * a + 2) * stride - 1;
-            const T left = tile[padded<PAD>(lo)];
-            const T right = tile[padded<PAD>(hi)];
-            tile[padded<PAD>(lo)] = right;
-            tile[padded<PAD>(hi)] = right + left;
-        }
-        __syncthreads();
-    }
+    for (int lv = kLdsLevels - 1; lv >= 0; --lv) tree_level<T, PAD, false>(tile, lv);
 #pragma unroll
     for (int k = 0; k < kLdsPerThread; ++k) {
         const int i = tid + k * kLdsThreads;

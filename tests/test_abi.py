@@ -112,7 +112,8 @@ def test_scan_validation(lib, fn):
 
 def test_ds_scan_validation(lib):
     assert lib.ds_scan(0, 2, 0, A, B, 10, None) == INV   # inclusive not 0/1
-    assert lib.ds_scan(0, 0, 3, A, B, 10, None) == INV   # bad algo
+    assert lib.ds_scan(0, 0, 4, A, B, 10, None) == INV   # bad algo
+    assert lib.ds_scan(3, 0, 3, A, B, 10, None) == DTY   # blocked layout: 4-byte types only
     assert lib.ds_scan(0, 0, -1, A, B, 10, None) == INV
     assert lib.ds_scan(2, 1, 2, A, A + 8, 10, None) == OVL
 
