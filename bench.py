@@ -326,6 +326,37 @@ def profile_pattern(args):
     log(f"profile run done: {args.pattern} x {args.steps}")
 
 
+def profile_radix(args):
+    """--profile-only --workload radix: 8-bit counting-sort passes over the
+    compaction keys (268,435,456 uint32), --steps each at shift 0, shift 24,
+    shift 0 again (so the order of the legs can be told from the digit),
+    then --steps key-value passes at shift 0; for counter runs."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import primitives_device_scan_amd as ds
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    nk = datagen.WORKLOADS["compact_256m"][0]
+    keys = torch.from_numpy(datagen.workload("compact_256m").view(np.int32)).to(dev)
+    vals = torch.from_numpy(datagen.keys_u32(8, nk).view(np.int32)).to(dev)
+    kout, vout = torch.empty_like(keys), torch.empty_like(vals)
+    for shift in (0, 24, 0):
+        for _ in range(max(1, args.steps)):
+            st = ds.lib.ds_radix_pass(keys.data_ptr(), kout.data_ptr(), None, None, nk, shift, 8, sh)
+            if st:
+                raise ds.DevscanError(st, "ds_radix_pass")
+    for _ in range(max(1, args.steps)):
+        st = ds.lib.ds_radix_pass(keys.data_ptr(), kout.data_ptr(), vals.data_ptr(), vout.data_ptr(), nk, 0, 8, sh)
+        if st:
+            raise ds.DevscanError(st, "ds_radix_pass kv")
+    torch.cuda.synchronize()
+    log("profile run done: radix passes")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +381,9 @@ def main():
                     help="with --profile-only: a 1 GiB read before every scan launch (the cold protocol)")
     ap.add_argument("--algo", default="default",
                     help="with --profile-only: the ds_scan algorithm the scans use (default, lookback_blocked, ...)")
+    ap.add_argument("--workload", default="scan", choices=["scan", "radix"],
+                    help="with --profile-only: radix = counting-sort passes over 2^28 keys (shift 0, then 24, then 0 "
+                         "again, --steps each; then --steps key-value passes)")
     ap.add_argument("--pattern", default=None,
                     help="with --profile-only: MODE:VPT:LAYOUT of ds_bandwidth_pattern to launch --steps times "
                          "instead of the scans (e.g. write:28:0)")
@@ -367,6 +401,8 @@ def main():
         return ceiling_experiment(args)
     if args.profile_only and args.pattern:
         return profile_pattern(args)
+    if args.profile_only and args.workload == "radix":
+        return profile_radix(args)
 
     import numpy as np
     import torch

@@ -39,16 +39,17 @@ __device__ __forceinline__ void wave_lds_sync()
 constexpr int kGroup = 8;  // vector indices per staging round: 8 KiB of LDS per wave
 
 // IN_A16: `in` is 16-byte aligned (whole waves load 16-byte vectors either way).
-template <typename T, bool IN_A16, int CMP>
-__global__ __launch_bounds__(kThreads, kCompactOcc) void compact_kernel(const T* in, T* out, int64_t* num_selected,
+// VPT vectors per thread, compiled for OCC workgroups per CU.
+template <typename T, bool IN_A16, int CMP, int VPT = kCompactVPT, int OCC = kCompactOcc>
+__global__ __launch_bounds__(kThreads, OCC) void compact_kernel(const T* in, T* out, int64_t* num_selected,
                                                                int64_t n, int64_t num_tiles, T operand, Ctrl* ctrl,
                                                                uint64_t* status, uint32_t spin_limit)
 {
-    using S = Shape<T, kCompactVPT>;
+    using S = Shape<T, VPT>;
     constexpr int V = S::kPerVec;
     constexpr int kBuf = kWave * V * kGroup + V;  // a round's slices plus the alignment shift
     constexpr int kMaskWords = (S::kItems + 63) / 64;  // a vector's V bits never straddle two words
-    static_assert(kCompactVPT % kGroup == 0, "whole rounds");
+    constexpr int kRounds = (VPT + kGroup - 1) / kGroup;  // the last round may be shorter
     __shared__ uint32_t s_wave[kWaves];
     __shared__ __attribute__((aligned(16))) T s_stage[kWaves][kBuf];
     const int lane = lane_id();
@@ -62,31 +63,52 @@ __global__ __launch_bounds__(kThreads, kCompactOcc) void compact_kernel(const T*
     const bool whole = seg + S::kWaveElems <= n;
     T e[S::kItems];
     if (whole)
-        load_vec<T, kCompactVPT, IN_A16>(in, seg, lane, e);
+        load_vec<T, VPT, IN_A16>(in, seg, lane, e);
     else
-        load_scalar<T, kCompactVPT>(in, seg, n, lane, e, T(0));
+        load_scalar<T, VPT>(in, seg, n, lane, e, T(0));
 
     uint64_t keepm[kMaskWords] = {};  // bit i % 64 of word i / 64: this lane keeps element slot i
 #pragma unroll
-    for (int k = 0; k < kCompactVPT; ++k)
+    for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             const int i = k * V + j;
             if ((whole || elem_index<T>(seg, k, j, lane) < n) && keep<CMP>(e[i], operand))
                 keepm[i / 64] |= 1ull << (i % 64);
         }
-    uint32_t cnt[kCompactVPT];
+    uint32_t cnt[VPT];
+    uint32_t mine = 0;
 #pragma unroll
-    for (int k = 0; k < kCompactVPT; ++k)
+    for (int k = 0; k < VPT; ++k) {
         cnt[k] = (uint32_t)__builtin_popcountll((keepm[k * V / 64] >> (k * V % 64)) & ((1ull << V) - 1));
-    uint32_t off[kCompactVPT];
-    uint32_t wave_excl;
-    const uint32_t agg = tile_local_scan<uint32_t, 1, kCompactVPT>(cnt, off, wave_excl, s_wave);
-    const uint32_t wave_total = s_wave[wave];
+        mine += cnt[k];
+    }
+    // The tile's keep count by a reduction first, published at once, so that
+    // successors can use it while this tile ranks its elements.
+    const uint32_t wave_total = wave_sum(mine);
+    if (lane == 0) s_wave[wave] = wave_total;
+    __syncthreads();
+    uint32_t agg = 0, wave_excl = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t v = s_wave[w];
+        if (w < wave) wave_excl += v;
+        agg += v;
+    }
+    if (num_tiles > 1 && threadIdx.x == 0) publish_early<uint32_t>(status, tile, epoch, agg, 0u);
+    // Rank of each vector's first kept element within the wave.
+    uint32_t off[VPT];
+    uint32_t run = 0;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const uint32_t incl = wave_inclusive_scan(cnt[k]);
+        off[k] = run + wave_shift_right1(incl);
+        run += readlane(incl, kWave - 1);
+    }
 
     uint32_t prefix = 0;
     if (num_tiles > 1)
-        prefix = tile_prefix<uint32_t>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit);
+        prefix = tile_prefix<uint32_t>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit, 0u, true);
 
     // A prefix past n can only come from a look-back that gave up; never write past the buffer.
     const bool fits = (int64_t)prefix + agg <= n;
@@ -97,13 +119,14 @@ __global__ __launch_bounds__(kThreads, kCompactOcc) void compact_kernel(const T*
     const uint32_t out_phase = (uint32_t)(((uintptr_t)out % kVecBytes) / sizeof(T));
     T* const stage = s_stage[wave];
 #pragma unroll
-    for (int g = 0; g < kCompactVPT; g += kGroup) {
+    for (int rd = 0; rd < kRounds; ++rd) {
+        const int g = rd * kGroup, gend = g + kGroup < VPT ? g + kGroup : VPT;
         const uint32_t start = readlane(off[g], 0);  // rank of the round's first kept element in the wave
-        const uint32_t end = g + kGroup < kCompactVPT ? readlane(off[g + kGroup], 0) : wave_total;
+        const uint32_t end = gend < VPT ? readlane(off[gend < VPT ? gend : 0], 0) : wave_total;  // index kept in range
         const int64_t first = wave_base + start;
         const uint32_t shift = (uint32_t)((first + out_phase) % V);
 #pragma unroll
-        for (int k = g; k < g + kGroup; ++k) {
+        for (int k = g; k < gend; ++k) {
             uint32_t r = off[k] - start + shift;
 #pragma unroll
             for (int j = 0; j < V; ++j)
@@ -150,7 +173,7 @@ template <typename T, int CMP>
 static hipError_t compact_cmp(const void* in, void* out, int64_t* num_selected, int64_t n, T operand,
                               const DevWs& ws, uint32_t spin, hipStream_t st)
 {
-    const int64_t tiles = (n + Shape<T, kCompactVPT>::kTile - 1) / Shape<T, kCompactVPT>::kTile;
+    const int64_t tiles = (n + Shape<T, kCompactVPT>::kTile - 1) / Shape<T, kCompactVPT>::kTile;  // compact_tile_elems
     if (tiles > 1 && (!ws.ctrl || !ws.status)) return hipErrorInvalidValue;  // several tiles need a workspace
     if (aligned16(in))
         compact_kernel<T, true, CMP><<<dim3((unsigned)tiles), dim3(kThreads), 0, st>>>(
