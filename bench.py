@@ -357,6 +357,49 @@ def profile_radix(args):
     log("profile run done: radix passes")
 
 
+def profile_compact(args):
+    """--profile-only --workload compact: --steps launches each of compact_if
+    (ordered), ds_compact_unordered with claims per wave and per workgroup over
+    the compaction keys (268,435,456 uint32, keep key < 2^31), then --steps
+    copies of 1 GiB (the counters' scale factor); for counter runs."""
+    import torch
+
+    import datagen
+    import primitives_device_scan_amd as ds
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    nk = datagen.WORKLOADS["compact_256m"][0]
+    keys = torch.from_numpy(datagen.workload("compact_256m").view("int32")).to(dev)
+    out = torch.empty_like(keys)
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+    evict = Evictor(torch, dev) if args.cold else (lambda: None)
+    for _ in range(max(1, args.steps)):
+        evict()
+        st = ds.lib.compact_if(ds.DS_UINT32, keys.data_ptr(), out.data_ptr(), cnt.data_ptr(), nk, ds.CMP["<"],
+                               1 << 31, sh)
+        if st:
+            raise ds.DevscanError(st, "compact_if")
+    for claim in (0, 1):
+        for _ in range(max(1, args.steps)):
+            evict()
+            st = ds.lib.ds_compact_unordered(ds.DS_UINT32, keys.data_ptr(), out.data_ptr(), cnt.data_ptr(), nk,
+                                             ds.CMP["<"], 1 << 31, claim, sh)
+            if st:
+                raise ds.DevscanError(st, "ds_compact_unordered")
+    for _ in range(max(1, args.steps)):
+        evict()
+        st = ds.lib.ds_copy(keys.data_ptr(), out.data_ptr(), nk * 4, sh)
+        if st:
+            raise ds.DevscanError(st, "ds_copy")
+    torch.cuda.synchronize()
+    if ds.query_timeout():
+        log("a look-back wait gave up")
+        sys.exit(1)
+    log("profile run done: compaction")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,9 +424,10 @@ def main():
                     help="with --profile-only: a 1 GiB read before every scan launch (the cold protocol)")
     ap.add_argument("--algo", default="default",
                     help="with --profile-only: the ds_scan algorithm the scans use (default, lookback_blocked, ...)")
-    ap.add_argument("--workload", default="scan", choices=["scan", "radix"],
+    ap.add_argument("--workload", default="scan", choices=["scan", "radix", "compact"],
                     help="with --profile-only: radix = counting-sort passes over 2^28 keys (shift 0, then 24, then 0 "
-                         "again, --steps each; then --steps key-value passes)")
+                         "again, --steps each; then --steps key-value passes); compact = compact_if, then "
+                         "ds_compact_unordered per wave and per workgroup, then 1 GiB copies, --steps each")
     ap.add_argument("--pattern", default=None,
                     help="with --profile-only: MODE:VPT:LAYOUT of ds_bandwidth_pattern to launch --steps times "
                          "instead of the scans (e.g. write:28:0)")
@@ -403,6 +447,8 @@ def main():
         return profile_pattern(args)
     if args.profile_only and args.workload == "radix":
         return profile_radix(args)
+    if args.profile_only and args.workload == "compact":
+        return profile_compact(args)
 
     import numpy as np
     import torch

@@ -423,9 +423,9 @@ __device__ T lookback(uint64_t* status, int64_t tile, uint32_t epoch, T agg, uin
         // the flag becomes visible before the (incomplete) prefix this tile publishes
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     };
+    uint32_t f = kFlagNone;
+    T v0 = T(0);
     for (;;) {
-        uint32_t f = kFlagPrefix;
-        T v0;
         if (lane == 0) f = C::read(status, tile - 1, epoch, v0);
         if (__builtin_amdgcn_readfirstlane(f) != kFlagNone) break;
         if (++polls >= spin_limit) {
@@ -434,8 +434,20 @@ __device__ T lookback(uint64_t* status, int64_t tile, uint32_t epoch, T agg, uin
         }
         __builtin_amdgcn_s_sleep(1);
     }
+    // The predecessor's word is already in hand: an inclusive prefix there ends
+    // the look-back without a window read (one status round trip fewer on the
+    // chain); an aggregate starts the sum and the window begins a tile further back.
     T acc = T(0);
     int64_t base = tile - 1;
+    f = __builtin_amdgcn_readfirstlane(f);
+    if (f != kFlagNone) {
+        acc = readlane(v0, 0);
+        if (f == kFlagPrefix) {
+            if (lane == 0) C::publish(status, tile, epoch, kFlagPrefix, acc + agg);
+            return acc;
+        }
+        base = tile - 2;
+    }
     for (;;) {
         const int64_t idx = base - lane;
         T v = T(0);
