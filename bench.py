@@ -264,7 +264,7 @@ def ceiling_experiment(args):
 
     rows = []
     for mode, mcode in ds._binding.PATTERNS.items():
-        moved = {"read": 1.0, "write": 1.0, "copy": 2.0, "read_half": 1.5}[mode]
+        moved = {"read": 1.0, "write": 1.0, "copy": 2.0, "read_half": 1.5, "read_half_held": 1.5, "copy_held": 2.0}[mode]
         for vpt in (1, 4, 16, 20, 28):
             for layout in (0, 1):
                 def fn():
@@ -293,10 +293,11 @@ def ceiling_experiment(args):
     keys = torch.ones(nk, dtype=torch.int32, device=dev)
     kout = torch.zeros_like(keys)
     cvpt = int(L.ds_tile_elems(ds.DS_UINT32, ds._binding.TILE_OF["compact"])) // 1024
-    hf = lambda: L.ds_bandwidth_pattern(3, cvpt, 0, keys.data_ptr(), kout.data_ptr(), nk * 4, sh)
-    hw, hc = warm_ms(hf), float(np.median(cold_times_ms(torch, stream, hf, evict, reps=10)))
-    out["compaction_shape_256m"] = {"kib_per_workgroup": 4 * cvpt, "bytes": int(nk * 6),
-                                    "warm_us": round(hw * 1e3, 1), "cold_us": round(hc * 1e3, 1)}
+    out["compaction_shape_256m"] = {"kib_per_workgroup": 4 * cvpt, "bytes": int(nk * 6)}
+    for mname, mcode in (("held", 4), ("streaming", 3)):
+        hf = lambda: L.ds_bandwidth_pattern(mcode, cvpt, 0, keys.data_ptr(), kout.data_ptr(), nk * 4, sh)
+        hw, hc = warm_ms(hf), float(np.median(cold_times_ms(torch, stream, hf, evict, reps=10)))
+        out["compaction_shape_256m"][mname] = {"warm_us": round(hw * 1e3, 1), "cold_us": round(hc * 1e3, 1)}
     print(json.dumps(out), flush=True)
 
 
@@ -590,6 +591,12 @@ def main():
     extras["copy_same_pattern_cold_gbs"] = round(alg_bytes / (cp_cold_ms * 1e-3) / 1e9, 1)
     extras["scan_over_copy"] = round(cp_ms / float(np.median(ms_i)), 4)
     extras["scan_over_copy_cold"] = round(cp_cold_ms / cold_ms, 4)
+    # the same tile held as the scan holds it: no store before the whole tile has arrived
+    svpt = int(L.ds_scan_tile_elems(ds.DS_INT32, 0, n)) * 4 // 4096
+    chf = lambda: L.ds_bandwidth_pattern(5, svpt, 0, d_xi.data_ptr(), d_yi.data_ptr(), n * 4 // 16 * 16, sh)
+    ch_cold_ms = float(np.median(cold_times_ms(torch, stream, chf, evict, reps=20)))
+    extras["copy_held_same_pattern_cold_gbs"] = round(alg_bytes / (ch_cold_ms * 1e-3) / 1e9, 1)
+    extras["scan_over_copy_held_cold"] = round(ch_cold_ms / cold_ms, 4)
     tp_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 0, ds.ALGO["three_pass"], d_xi.data_ptr(), d_yi.data_ptr(), n, sh))
     extras["three_pass_int32_gelem_s"] = round(n / (tp_ms * 1e-3) / 1e9, 2)
     extras["three_pass_int32_alg_gbs"] = round(alg_bytes / (tp_ms * 1e-3) / 1e9, 1)
@@ -671,11 +678,16 @@ def main():
         kept = int(cnt.item())
         cbytes = nk * 4 + kept * 4
         extras["compact_256m_us"] = round(c_ms * 1e3, 1)
-        # its ceiling: the same tile and grid reading every key and writing half of them, no scan
+        # its ceiling: the same tile and grid reading every key and writing half of them, no scan,
+        # held as a single pass must hold it (no store before the whole tile has arrived); and the
+        # same bytes streamed (the stored half loaded last and stored at once), for context
         cvpt = int(L.ds_tile_elems(ds.DS_UINT32, ds._binding.TILE_OF["compact"])) * 4 // 4096
-        h_ms = timed(lambda: L.ds_bandwidth_pattern(3, cvpt, 0, keys.data_ptr(), kout.data_ptr(), nk * 4, sh), reps=10)
+        h_ms = timed(lambda: L.ds_bandwidth_pattern(4, cvpt, 0, keys.data_ptr(), kout.data_ptr(), nk * 4, sh), reps=10)
+        hs_ms = timed(lambda: L.ds_bandwidth_pattern(3, cvpt, 0, keys.data_ptr(), kout.data_ptr(), nk * 4, sh), reps=10)
         extras["compact_ceiling_256m_us"] = round(h_ms * 1e3, 1)
         extras["compact_over_ceiling"] = round(h_ms / c_ms, 4)
+        extras["compact_streaming_256m_us"] = round(hs_ms * 1e3, 1)
+        extras["compact_over_streaming"] = round(hs_ms / c_ms, 4)
         extras["compact_256m_gelem_s"] = round(nk / (c_ms * 1e-3) / 1e9, 2)
         extras["compact_256m_alg_gbs"] = round(cbytes / (c_ms * 1e-3) / 1e9, 1)
         # the order-free form: atomic space claims per wave (the pages') and per workgroup

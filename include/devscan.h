@@ -260,8 +260,11 @@ typedef enum {
     DS_PATTERN_READ = 0,       /* read nbytes (folded on chip; nothing written) */
     DS_PATTERN_WRITE = 1,      /* write nbytes (d_in unused, may be NULL) */
     DS_PATTERN_COPY = 2,       /* read then write each tile: the held tile of the look-back scan */
-    DS_PATTERN_READ_HALF = 3   /* read each tile, write its first half contiguously: compaction's bytes
-                                  at half kept, with no scan */
+    DS_PATTERN_READ_HALF = 3,  /* read each tile, write its first half contiguously: compaction's bytes
+                                  at half kept, with no scan (stores may leave as their loads arrive) */
+    DS_PATTERN_READ_HALF_HELD = 4, /* as READ_HALF, but no store leaves before the whole tile has arrived,
+                                      as in a single-pass compaction, which stores only after its prefix */
+    DS_PATTERN_COPY_HELD = 5   /* as COPY, held the same way: the look-back scan's structure */
 } ds_pattern;
 
 /*

@@ -36,7 +36,7 @@ EXPORTS = ["scan_exclusive", "scan_inclusive", "ds_scan", "ds_scan_seeded", "ds_
 TILE_OF = {"scan_exclusive": 0, "scan_inclusive": 1, "three_pass": 2, "compact": 3, "lds_tile_scan": 4,
            "counting_sort": 5, "counting_sort_values": 6, "moe_align": 7}
 TILE_VARIANTS = {"tree": 0, "tree_pad1": 1, "tree_pad2": 2, "hillis_steele": 3}
-PATTERNS = {"read": 0, "write": 1, "copy": 2, "read_half": 3}
+PATTERNS = {"read": 0, "write": 1, "copy": 2, "read_half": 3, "read_half_held": 4, "copy_held": 5}
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:

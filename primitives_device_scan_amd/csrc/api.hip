@@ -418,7 +418,7 @@ int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream)
 int ds_bandwidth_pattern(int mode, int vectors_per_thread, int layout, const void* d_in, void* d_out, int64_t nbytes,
                          hipStream_t stream)
 {
-    if (mode < 0 || mode > 3 || layout < 0 || layout > 1 || !ds::pattern_vpt_ok(vectors_per_thread))
+    if (mode < 0 || mode > 5 || layout < 0 || layout > 1 || !ds::pattern_vpt_ok(vectors_per_thread))
         return DS_ERR_INVALID_VALUE;
     if (nbytes < 0 || (nbytes % 16)) return DS_ERR_INVALID_VALUE;
     if (nbytes == 0) return DS_OK;

@@ -25,18 +25,14 @@ __device__ __forceinline__ bool keep(T v, T c)
 // Compaction over 64 KiB tiles. The keep flags live as one bit per element in
 // 64-bit mask words; the per-vector keep counts go through the same
 // wave/tile scan and look-back as a scan of 32-bit counts. Once the tile's
-// output offset is known, each wave moves its kept elements out in rounds of
-// kGroup vector indices: the kept elements of those slices are packed into a
-// per-wave LDS buffer at their rank -- shifted so that LDS index and output
-// index agree modulo a 16-byte vector -- and written back as one contiguous
-// run of 16-byte non-temporal stores (element stores at the two ragged ends).
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-}
-
-constexpr int kGroup = 8;  // vector indices per staging round: 8 KiB of LDS per wave
+// output offset is known, the kept elements leave through one LDS buffer in
+// windows of the tile's ranks: every wave places the kept elements whose rank
+// falls in the window -- shifted so that LDS index and output index agree
+// modulo a 64-byte line -- and the whole workgroup writes the window back as
+// one contiguous run of 16-byte non-temporal stores (element stores at the two
+// ragged ends), each wave's store covering whole lines. At up to kWinBytes of kept data per tile that is one window, so
+// a tile's output has seams only where it meets its neighbours.
+constexpr int kWinBytes = 36 * 1024;  // LDS for one window; 4 workgroups per CU still fit
 
 // IN_A16: `in` is 16-byte aligned (whole waves load 16-byte vectors either way).
 // VPT vectors per thread, compiled for OCC workgroups per CU.
@@ -47,11 +43,11 @@ __global__ __launch_bounds__(kThreads, OCC) void compact_kernel(const T* in, T* 
 {
     using S = Shape<T, VPT>;
     constexpr int V = S::kPerVec;
-    constexpr int kBuf = kWave * V * kGroup + V;  // a round's slices plus the alignment shift
+    constexpr uint32_t kWin = kWinBytes / sizeof(T);  // ranks per window, a multiple of V
     constexpr int kMaskWords = (S::kItems + 63) / 64;  // a vector's V bits never straddle two words
-    constexpr int kRounds = (VPT + kGroup - 1) / kGroup;  // the last round may be shorter
     __shared__ uint32_t s_wave[kWaves];
-    __shared__ __attribute__((aligned(16))) T s_stage[kWaves][kBuf];
+    constexpr uint32_t kLine = 64 / sizeof(T);  // elements per 64-byte line
+    __shared__ __attribute__((aligned(16))) T s_stage[kWin + kLine];  // a window plus the alignment shift
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
     const int64_t tile = blockIdx.x;
@@ -96,9 +92,9 @@ __global__ __launch_bounds__(kThreads, OCC) void compact_kernel(const T* in, T* 
         agg += v;
     }
     if (num_tiles > 1 && threadIdx.x == 0) publish_early<uint32_t>(status, tile, epoch, agg, 0u);
-    // Rank of each vector's first kept element within the wave.
+    // Tile rank of each vector's first kept element in this lane.
     uint32_t off[VPT];
-    uint32_t run = 0;
+    uint32_t run = wave_excl;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const uint32_t incl = wave_inclusive_scan(cnt[k]);
@@ -113,42 +109,42 @@ __global__ __launch_bounds__(kThreads, OCC) void compact_kernel(const T* in, T* 
     // A prefix past n can only come from a look-back that gave up; never write past the buffer.
     const bool fits = (int64_t)prefix + agg <= n;
     if (!fits && threadIdx.x == 0) flag_timeout(ctrl);
-    const int64_t wave_base = (int64_t)prefix + wave_excl;  // output index of this wave's first kept element
-    // Elements of `out` before its first 16-byte boundary's phase: the runs are
-    // staged so that every full vector written lands 16-byte aligned.
-    const uint32_t out_phase = (uint32_t)(((uintptr_t)out % kVecBytes) / sizeof(T));
-    T* const stage = s_stage[wave];
+    // Phase of `out` within a 64-byte line, in elements: a window is staged so
+    // that its slot 0 lands on a line boundary (a wave's 1 KiB store then
+    // writes 16 whole lines, not parts of 17).
+    const uint32_t out_phase = (uint32_t)(((uintptr_t)out % 64) / sizeof(T));
+    for (uint32_t lo = 0; lo < agg; lo += kWin) {  // agg is the same in every wave
+        const uint32_t hi = agg - lo < kWin ? agg : lo + kWin;
+        const int64_t first = (int64_t)prefix + lo;  // output index of the window's first element
+        const uint32_t shift = (uint32_t)((first + out_phase) % kLine);
+        const uint32_t width = hi - lo;
 #pragma unroll
-    for (int rd = 0; rd < kRounds; ++rd) {
-        const int g = rd * kGroup, gend = g + kGroup < VPT ? g + kGroup : VPT;
-        const uint32_t start = readlane(off[g], 0);  // rank of the round's first kept element in the wave
-        const uint32_t end = gend < VPT ? readlane(off[gend < VPT ? gend : 0], 0) : wave_total;  // index kept in range
-        const int64_t first = wave_base + start;
-        const uint32_t shift = (uint32_t)((first + out_phase) % V);
-#pragma unroll
-        for (int k = g; k < gend; ++k) {
-            uint32_t r = off[k] - start + shift;
+        for (int k = 0; k < VPT; ++k) {
+            uint32_t t = off[k] - lo;  // window slot of the vector's first kept element; wraps below the window
 #pragma unroll
             for (int j = 0; j < V; ++j)
-                if ((keepm[(k * V + j) / 64] >> ((k * V + j) % 64)) & 1ull) stage[r++] = e[k * V + j];
+                if ((keepm[(k * V + j) / 64] >> ((k * V + j) % 64)) & 1ull) {
+                    if (t < width) s_stage[t + shift] = e[k * V + j];
+                    ++t;
+                }
         }
-        wave_lds_sync();
-        const uint32_t span = shift + (end - start);  // staged slots, the shift included
-        // Output index of staged slot 0: out + dst0 is 16-byte aligned; dst0 may be
+        __syncthreads();
+        const uint32_t span = shift + width;  // staged slots, the shift included
+        // Output index of staged slot 0: out + dst0 is 64-byte aligned; dst0 may be
         // below 0, and only slots from `shift` on (indices from `first`) are written.
         const int64_t dst0 = first - (int64_t)shift;
         if (fits) {
-            for (uint32_t q = (uint32_t)lane * V; q < span; q += kWave * V) {
+            for (uint32_t q = threadIdx.x * V; q < span; q += kThreads * V) {
                 if (q >= shift && q + V <= span) {
-                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + q),
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(s_stage + q),
                                                 reinterpret_cast<u32x4*>(out + (dst0 + q)));
                 } else {
                     for (uint32_t i = q; i < q + V && i < span; ++i)
-                        if (i >= shift) out[dst0 + i] = stage[i];
+                        if (i >= shift) out[dst0 + i] = s_stage[i];
                 }
             }
         }
-        wave_lds_sync();
+        if (hi < agg) __syncthreads();  // the next window reuses the buffer
     }
     if (tile == num_tiles - 1 && threadIdx.x == 0) {
         // -1 when a look-back wait gave up (here or in a tile whose prefix

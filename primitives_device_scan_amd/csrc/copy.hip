@@ -45,6 +45,10 @@ hipError_t launch_copy(const void* in, void* out, int64_t nbytes, hipStream_t st
 //        3 compaction-shaped: read the whole tile, write its first half
 //          contiguously at out + tile * (tile bytes / 2): the bytes
 //          compact_if moves when half the elements are kept, with no scan
+//        4 as 3, held: every store depends on a fold of every loaded vector,
+//          so no store leaves before the whole tile has arrived (a single-pass
+//          compaction cannot store before its prefix, which needs the tile)
+//        5 as 2, held the same way (the look-back scan's structure)
 //   LAYOUT 0 contiguous tile, lane l of wave w holding vectors k * 64 + l of
 //            the wave's quarter (the scan's tile)
 //          1 four-KiB chunks at a 32 KiB stride: a group of 8 consecutive
@@ -64,6 +68,30 @@ __device__ __forceinline__ void pattern_body(const u32x4* in, u32x4* out, int64_
 #pragma unroll
         for (int k = 0; k < VPT; ++k)
             r[k] = (WHOLE || addr[k] < nvec) ? __builtin_nontemporal_load(in + addr[k]) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (MODE == 4 || MODE == 5) {
+        // the fold of all VPT vectors gates every store; `magic` never matches real data
+        // in a way that matters here (a bandwidth probe: a match flips one bit)
+        uint32_t acc = 0;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+            if (WHOLE || addr[k] < nvec) acc ^= r[k].x ^ r[k].y ^ r[k].z ^ r[k].w;
+        const uint32_t z = acc == magic ? 1u : 0u;
+        const int64_t half = (int64_t)kThreads * VPT / 2;
+        const int64_t dst0 = (int64_t)blockIdx.x * half;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            u32x4 v = r[k];
+            v.x ^= z;
+            if constexpr (MODE == 4) {
+                const int64_t q = (int64_t)k * kThreads + threadIdx.x;
+                if (q < half && (WHOLE || (dst0 + q < nvec && addr[k] < nvec)))
+                    __builtin_nontemporal_store(v, out + dst0 + q);
+            } else {
+                if (WHOLE || addr[k] < nvec) __builtin_nontemporal_store(v, out + addr[k]);
+            }
+        }
+        return;
     }
     if constexpr (MODE == 0 || MODE == 3) {
         // every loaded vector not stored below is folded into one word, so no load is dead
@@ -160,7 +188,9 @@ hipError_t launch_pattern(int mode, int vpt, int layout, const void* in, void* o
     case 0: return pattern_mode<0>(vpt, layout, in, out, nvec, stream);
     case 1: return pattern_mode<1>(vpt, layout, in, out, nvec, stream);
     case 2: return pattern_mode<2>(vpt, layout, in, out, nvec, stream);
-    default: return pattern_mode<3>(vpt, layout, in, out, nvec, stream);
+    case 3: return pattern_mode<3>(vpt, layout, in, out, nvec, stream);
+    case 4: return pattern_mode<4>(vpt, layout, in, out, nvec, stream);
+    default: return pattern_mode<5>(vpt, layout, in, out, nvec, stream);
     }
 }
 

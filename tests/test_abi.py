@@ -207,7 +207,8 @@ def test_copy_validation(lib):
 
 def test_bandwidth_pattern_validation(lib):
     f = lib.ds_bandwidth_pattern
-    assert f(4, 1, 0, A, B, 4096, None) == INV       # bad mode
+    assert f(6, 1, 0, A, B, 4096, None) == INV       # bad mode
+    assert f(-1, 1, 0, A, B, 4096, None) == INV
     assert f(0, 3, 0, A, B, 4096, None) == INV       # vectors per thread not offered
     assert f(0, 1, 2, A, B, 4096, None) == INV       # bad layout
     assert f(0, 1, 0, A, B, 4100, None) == INV       # not whole vectors
