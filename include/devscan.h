@@ -158,8 +158,8 @@ int ds_scan_seeded(int dtype, int inclusive, const void* d_in, void* d_out, int6
  * allocating routine: its control block and status words live in a fixed
  * 4 MiB array in the library's own device memory, one per GPU, held until the
  * process ends, with room for 32,766 tiles (n up to 671M 4-byte integers,
- * 1.07G fp32 for the exclusive scan, 671M fp32 inclusive, 469M 8-byte
- * elements at least; DS_ERR_TOO_LARGE beyond). Every call on a GPU shares
+ * 1.07G fp32, 469M 8-byte elements at least; DS_ERR_TOO_LARGE beyond). Every
+ * call on a GPU shares
  * that GPU's array, so calls that overlap in time on one GPU (different
  * streams, no ordering between them) race and give wrong results; order them
  * on one stream. The first call on a device enqueues a kernel that clears

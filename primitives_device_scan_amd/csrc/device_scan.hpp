@@ -11,14 +11,14 @@ namespace ds {
 // 16-byte vectors per thread (VPT); a tile is 256 threads x VPT x 16 B.
 //  - look-back scan: large tiles, since resident tile bytes per CU are what
 //    hide the look-back latency (several microseconds under full HBM load)
-//    behind other tiles' transfers. 4-byte integers and fp32 inclusive: 80 KiB
-//    tiles (20 vectors per thread, 131-145 VGPRs, no spill) at 3 workgroups
-//    per CU. Measured on MI355X at n = 100M with the status words padded to a
-//    line each, 80-128 KiB integer tiles (3 or 2 per CU) take 138-141 us,
-//    144 KiB ones 142 us; 112 KiB at 3 per CU spill and lose 5-8 us after a
-//    cache eviction. fp32 exclusive: 128 KiB tiles (32 vectors, 205 VGPRs) at
-//    2 per CU take 137.3-137.8 us after an eviction against 139.2-140.0 us at
-//    80 KiB (112 and 144 KiB: 141-143 us).
+//    behind other tiles' transfers. 4-byte integers: 80 KiB tiles (20 vectors
+//    per thread, 131-145 VGPRs, no spill) at 3 workgroups per CU. Measured on
+//    MI355X at n = 100M with the status words padded to a line each, 80-128 KiB
+//    integer tiles (3 or 2 per CU) take 138-141 us, 144 KiB ones 142 us; 112 KiB
+//    at 3 per CU spill and lose 5-8 us after a cache eviction. fp32: 128 KiB
+//    tiles (32 vectors, 205 VGPRs) at 2 per CU take 136-138 us after an
+//    eviction, exclusive or inclusive, against 139-141 us at 80 KiB (112 and
+//    144 KiB: 141-143 us).
 //    8-byte types: 144 / 112 KiB tiles (exclusive / inclusive) at 2 per CU
 //    (ScanOcc); 96-112 KiB at 3 per CU spill and were slower, 128 KiB 1% slower;
 //  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
@@ -33,9 +33,7 @@ struct IsFloat<float> {
 };
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
-    static constexpr int value = sizeof(T) == 8              ? (INCLUSIVE ? 28 : 36)
-                                 : (IsFloat<T>::value && !INCLUSIVE) ? 32
-                                                                     : 20;
+    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 36) : IsFloat<T>::value ? 32 : 20;
 };
 // Workgroups per CU the look-back kernel is compiled for (waves per SIMD):
 // tiles past 80 KiB need up to 256 VGPRs; every other tile fits 3.
