@@ -268,7 +268,7 @@ def ceiling_experiment(args):
     rows = []
     for mode, mcode in ds._binding.PATTERNS.items():
         moved = {"read": 1.0, "write": 1.0, "copy": 2.0, "read_half": 1.5, "read_half_held": 1.5, "copy_held": 2.0}[mode]
-        for vpt in (1, 4, 16, 20, 28):
+        for vpt in (1, 4, 16, 20, 28, 32):
             for layout in (0, 1):
                 def fn():
                     st = L.ds_bandwidth_pattern(mcode, vpt, layout, a.data_ptr(), b.data_ptr(), nbytes, sh)
@@ -594,12 +594,14 @@ def main():
     extras["copy_same_pattern_cold_gbs"] = round(alg_bytes / (cp_cold_ms * 1e-3) / 1e9, 1)
     extras["scan_over_copy"] = round(cp_ms / float(np.median(ms_i)), 4)
     extras["scan_over_copy_cold"] = round(cp_cold_ms / cold_ms, 4)
-    # the same tile held as the scan holds it: no store before the whole tile has arrived
-    svpt = int(L.ds_scan_tile_elems(ds.DS_INT32, 0, n)) * 4 // 4096
-    chf = lambda: L.ds_bandwidth_pattern(5, svpt, 0, d_xi.data_ptr(), d_yi.data_ptr(), n * 4 // 16 * 16, sh)
-    ch_cold_ms = float(np.median(cold_times_ms(torch, stream, chf, evict, reps=20)))
-    extras["copy_held_same_pattern_cold_gbs"] = round(alg_bytes / (ch_cold_ms * 1e-3) / 1e9, 1)
-    extras["scan_over_copy_held_cold"] = round(ch_cold_ms / cold_ms, 4)
+    # each type's tile held as the scan holds it: no store before the whole tile has arrived
+    for name, dcode in (("int32", ds.DS_INT32), ("fp32", ds.DS_FP32)):
+        svpt = int(L.ds_scan_tile_elems(dcode, 0, n)) * 4 // 4096
+        chf = lambda: L.ds_bandwidth_pattern(5, svpt, 0, d_xi.data_ptr(), d_yi.data_ptr(), n * 4 // 16 * 16, sh)
+        ch_cold_ms = float(np.median(cold_times_ms(torch, stream, chf, evict, reps=20)))
+        key = "" if name == "int32" else "_fp32_tile"
+        extras[f"copy_held{key}_same_pattern_cold_gbs"] = round(alg_bytes / (ch_cold_ms * 1e-3) / 1e9, 1)
+        extras[f"{name}_scan_over_copy_held_cold"] = round(ch_cold_ms / float(np.median(cold[name])), 4)
     tp_ms = timed(lambda: L.ds_scan(ds.DS_INT32, 0, ds.ALGO["three_pass"], d_xi.data_ptr(), d_yi.data_ptr(), n, sh))
     extras["three_pass_int32_gelem_s"] = round(n / (tp_ms * 1e-3) / 1e9, 2)
     extras["three_pass_int32_alg_gbs"] = round(alg_bytes / (tp_ms * 1e-3) / 1e9, 1)

@@ -157,9 +157,8 @@ int ds_scan_seeded(int dtype, int inclusive, const void* d_in, void* d_out, int6
  * capture, tight serving loops, harnesses that forbid hipMalloc. It calls no
  * allocating routine: its control block and status words live in a fixed
  * 4 MiB array in the library's own device memory, one per GPU, held until the
- * process ends, with room for 32,766 tiles (n up to 671M 4-byte integers,
- * 1.07G fp32, 469M 8-byte elements at least; DS_ERR_TOO_LARGE beyond). Every
- * call on a GPU shares
+ * process ends, with room for 32,766 tiles (n up to 1.07G 4-byte and at least
+ * 469M 8-byte elements; DS_ERR_TOO_LARGE beyond). Every call on a GPU shares
  * that GPU's array, so calls that overlap in time on one GPU (different
  * streams, no ordering between them) race and give wrong results; order them
  * on one stream. The first call on a device enqueues a kernel that clears
@@ -249,9 +248,9 @@ int ds_moe_align(const int32_t* d_topk_ids, int64_t n, int num_experts, int bloc
 
 /*
  * Copy of nbytes from d_in to d_out with the same launch shape, 16-byte
- * accesses and tile size as the 4-byte scan: the practical bandwidth ceiling
- * the scan is measured against (the "copy, no scan" row of "Day 32 -- The
- * CUDA scan algorithm", section "Results"). nbytes must be a multiple of 16
+ * accesses and tile size (128 KiB) as the 4-byte scan: the practical
+ * bandwidth ceiling the scan is measured against (the "copy, no scan" row of
+ * "Day 32 -- The CUDA scan algorithm", section "Results"). nbytes must be a multiple of 16
  * and both pointers 16-byte aligned; the buffers must not overlap.
  */
 int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream);
@@ -260,7 +259,7 @@ int ds_copy(const void* d_in, void* d_out, int64_t nbytes, hipStream_t stream);
 typedef enum {
     DS_PATTERN_READ = 0,       /* read nbytes (folded on chip; nothing written) */
     DS_PATTERN_WRITE = 1,      /* write nbytes (d_in unused, may be NULL) */
-    DS_PATTERN_COPY = 2,       /* read then write each tile: the held tile of the look-back scan */
+    DS_PATTERN_COPY = 2,       /* read then write each tile (stores may leave as their loads arrive) */
     DS_PATTERN_READ_HALF = 3,  /* read each tile, write its first half contiguously: compaction's bytes
                                   at half kept, with no scan (stores may leave as their loads arrive) */
     DS_PATTERN_READ_HALF_HELD = 4, /* as READ_HALF, but no store leaves before the whole tile has arrived,
@@ -272,7 +271,7 @@ typedef enum {
  * Bandwidth probe for the ceiling table the scan and the compaction are read
  * against (the "copy, no scan" row of "Day 32 -- The CUDA scan algorithm",
  * section "Results", widened to reads, writes and tile sizes): 256-thread
- * workgroups each move vectors_per_thread (1, 2, 4, 8, 16, 20 or 28) 16-byte
+ * workgroups each move vectors_per_thread (1, 2, 4, 8, 16, 20, 28 or 32) 16-byte
  * vectors per thread with non-temporal accesses. layout 0: each workgroup a
  * contiguous tile, laid out as the scan's (lane l of wave w holds vectors
  * k * 64 + l of the wave's quarter); layout 1: 4 KiB chunks at a 32 KiB

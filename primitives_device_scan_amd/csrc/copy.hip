@@ -171,13 +171,14 @@ static hipError_t pattern_mode(int vpt, int layout, const void* in, void* out, i
     case 16: return pattern_launch<MODE, 16>(layout, in, out, nvec, st);
     case 20: return pattern_launch<MODE, 20>(layout, in, out, nvec, st);
     case 28: return pattern_launch<MODE, 28>(layout, in, out, nvec, st);
+    case 32: return pattern_launch<MODE, 32>(layout, in, out, nvec, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 bool pattern_vpt_ok(int vpt)
 {
-    return vpt == 1 || vpt == 2 || vpt == 4 || vpt == 8 || vpt == 16 || vpt == 20 || vpt == 28;
+    return vpt == 1 || vpt == 2 || vpt == 4 || vpt == 8 || vpt == 16 || vpt == 20 || vpt == 28 || vpt == 32;
 }
 
 hipError_t launch_pattern(int mode, int vpt, int layout, const void* in, void* out, int64_t nbytes,

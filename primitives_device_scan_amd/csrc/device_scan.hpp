@@ -11,29 +11,21 @@ namespace ds {
 // 16-byte vectors per thread (VPT); a tile is 256 threads x VPT x 16 B.
 //  - look-back scan: large tiles, since resident tile bytes per CU are what
 //    hide the look-back latency (several microseconds under full HBM load)
-//    behind other tiles' transfers. 4-byte integers: 80 KiB tiles (20 vectors
-//    per thread, 131-145 VGPRs, no spill) at 3 workgroups per CU. Measured on
-//    MI355X at n = 100M with the status words padded to a line each, 80-128 KiB
-//    integer tiles (3 or 2 per CU) take 138-141 us, 144 KiB ones 142 us; 112 KiB
-//    at 3 per CU spill and lose 5-8 us after a cache eviction. fp32: 128 KiB
-//    tiles (32 vectors, 205 VGPRs) at 2 per CU take 136-138 us after an
-//    eviction, exclusive or inclusive, against 139-141 us at 80 KiB (112 and
-//    144 KiB: 141-143 us).
+//    behind other tiles' transfers. 4-byte types: 128 KiB tiles (32 vectors
+//    per thread, 204-211 VGPRs, no spill) at 2 workgroups per CU. Measured on
+//    MI355X at n = 100M with the status words padded to a line each and the
+//    scanned values pinned before the look-back (scan_lookback.hip): 136-138 us
+//    after a cache eviction for int32 and fp32 alike, against 139-141 us for
+//    80 KiB tiles at 3 per CU, the earlier choice; 112 and 144 KiB tiles took
+//    141-143 us, and 112 KiB at 3 per CU spills. A held copy shows the same
+//    order: 135 us at 128 KiB and 2 per CU, 143-144 us at 80-112 KiB and 3-4.
 //    8-byte types: 144 / 112 KiB tiles (exclusive / inclusive) at 2 per CU
 //    (ScanOcc); 96-112 KiB at 3 per CU spill and were slower, 128 KiB 1% slower;
 //  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
 //    wait to hide; compaction's keep mask holds 64 elements).
-template <typename T>
-struct IsFloat {
-    static constexpr bool value = false;
-};
-template <>
-struct IsFloat<float> {
-    static constexpr bool value = true;
-};
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
-    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 36) : IsFloat<T>::value ? 32 : 20;
+    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 36) : 32;
 };
 // Workgroups per CU the look-back kernel is compiled for (waves per SIMD):
 // tiles past 80 KiB need up to 256 VGPRs; every other tile fits 3.
@@ -41,7 +33,7 @@ template <typename T, int VPT>
 struct ScanOcc {
     static constexpr int value = (VPT > 20 && (sizeof(T) == 8 || VPT > 28)) ? 2 : 3;
 };
-constexpr int kVPT = 20;  // the 4-byte scan tile: the same-pattern copy (ds_copy) uses it
+constexpr int kVPT = 32;  // the 4-byte scan tile: the same-pattern copy (ds_copy) uses it
 constexpr int kThreePassVPT = 16;
 constexpr int kCompactVPT = 16;
 constexpr int kCompactOcc = 4;  // workgroups per CU the ordered compaction is compiled for

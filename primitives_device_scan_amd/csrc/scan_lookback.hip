@@ -47,6 +47,12 @@ __global__ __launch_bounds__(kThreads, (ScanOcc<T, VPT>::value)) void lookback_s
     const T first = (seed != nullptr && tile == 0) ? *seed : T(0);
     if (num_tiles > 1 && threadIdx.x == 0) publish_early<T>(status, tile, epoch, agg, first);
     scan_in_wave<T, V, VPT, INCLUSIVE>(e);
+    // Left to itself the compiler sinks the integer scan's last additions past
+    // the wait below, into the prefix add (v_add3); done after the prefix
+    // arrives, they delay the stores: int32 at n = 100M took 140.0-140.6 us
+    // cold that way against 136.8-138.0 us pinned. The 8-byte exclusive tile
+    // (144 KiB) spills 28 bytes per lane when pinned and is left as it is.
+    if constexpr (sizeof(T) == 4 || INCLUSIVE) pin_in_registers(e);
     const T prefix =
         num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit, first, true) : first;
     add_uniform(e, prefix + wave_excl);

@@ -106,6 +106,18 @@ __device__ __forceinline__ T wave_shift_right1(T x) { return dpp<0x138>(x); }
 template <typename T>
 __device__ __forceinline__ T wave_sum(T x) { return readlane(wave_inclusive_scan(x), kWave - 1); }
 
+// An empty asm statement that claims to modify each value: the arithmetic
+// that produced them must be done here, before whatever follows. Used after a
+// tile's in-register scan so that the compiler cannot sink the scan's last
+// additions past the wait for the tile's prefix (folding them into the
+// prefix add), which would lengthen the time the tile is held.
+template <typename T, int N>
+__device__ __forceinline__ void pin_in_registers(T (&x)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // ---------------------------------------------------------------------------

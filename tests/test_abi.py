@@ -80,7 +80,7 @@ def test_scan_noalloc_validation(lib):
     assert f(0, 0, A + 2, B, 10, None) == MIS
     assert f(0, 0, A, A + 4, 10, None) == OVL
     far = A + (16 << 30)                           # no overlap with A at these sizes
-    assert f(0, 0, A, far, 1_000_000_000, None) == BIG   # more tiles than the fixed scratch holds
+    assert f(0, 0, A, far, 1_200_000_000, None) == BIG   # more tiles than the fixed scratch holds
     assert f(3, 1, A, far, 600_000_000, None) == BIG
 
 

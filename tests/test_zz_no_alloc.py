@@ -67,6 +67,6 @@ def test_noalloc_other_types_and_sizes():
     _check(x, False, "int32 n=100000007")
     # a size beyond the fixed array is refused before any launch; the next call works
     xin = to_dev(datagen.uniform_int(86, 16, 0, 9))
-    st = ds.lib.ds_scan_noalloc(0, 0, xin.data_ptr(), xin.data_ptr(), 1_000_000_000, stream_handle())
+    st = ds.lib.ds_scan_noalloc(0, 0, xin.data_ptr(), xin.data_ptr(), 1_200_000_000, stream_handle())
     assert st == ds.DS_ERR_TOO_LARGE
     _check(datagen.uniform_int(87, 333_333, 0, 100), True, "int32 n=333333 after a refused call")
