@@ -36,14 +36,14 @@ constexpr int kWinBytes = 36 * 1024;  // LDS for one window; 4 workgroups per CU
 
 // IN_A16: `in` is 16-byte aligned (whole waves load 16-byte vectors either way).
 // VPT vectors per thread, compiled for OCC workgroups per CU.
-template <typename T, bool IN_A16, int CMP, int VPT = kCompactVPT, int OCC = kCompactOcc>
+template <typename T, bool IN_A16, int CMP, int VPT = kCompactVPT, int OCC = kCompactOcc, int WIN_BYTES = kWinBytes>
 __global__ __launch_bounds__(kThreads, OCC) void compact_kernel(const T* in, T* out, int64_t* num_selected,
                                                                int64_t n, int64_t num_tiles, T operand, Ctrl* ctrl,
                                                                uint64_t* status, uint32_t spin_limit)
 {
     using S = Shape<T, VPT>;
     constexpr int V = S::kPerVec;
-    constexpr uint32_t kWin = kWinBytes / sizeof(T);  // ranks per window, a multiple of V
+    constexpr uint32_t kWin = WIN_BYTES / sizeof(T);  // ranks per window, a multiple of V
     constexpr int kMaskWords = (S::kItems + 63) / 64;  // a vector's V bits never straddle two words
     __shared__ uint32_t s_wave[kWaves];
     constexpr uint32_t kLine = 64 / sizeof(T);  // elements per 64-byte line
