@@ -24,14 +24,16 @@ __device__ __forceinline__ bool keep(T v, T c)
 
 // Compaction over 64 KiB tiles. The keep flags live as one bit per element in
 // 64-bit mask words; the per-vector keep counts go through the same
-// wave/tile scan and look-back as a scan of 32-bit counts. Once the tile's
-// output offset is known, the kept elements leave through one LDS buffer in
-// windows of the tile's ranks: every wave places the kept elements whose rank
-// falls in the window -- shifted so that LDS index and output index agree
-// modulo a 64-byte line -- and the whole workgroup writes the window back as
-// one contiguous run of 16-byte non-temporal stores (element stores at the two
-// ragged ends), each wave's store covering whole lines. At up to kWinBytes of kept data per tile that is one window, so
-// a tile's output has seams only where it meets its neighbours.
+// wave/tile scan and look-back as a scan of 32-bit counts. The tile's kept
+// elements leave through one LDS buffer in windows of the tile's ranks:
+// every wave places the kept elements whose rank falls in the window at LDS
+// index rank - window start (the first window before the look-back, while the
+// tile waits for its prefix), and once the output offset is known the whole
+// workgroup writes the window back as one contiguous run of 16-byte
+// non-temporal stores from a 64-byte line boundary (element stores at the two
+// ragged ends), each wave's store covering whole lines. At up to kWinBytes of
+// kept data per tile that is one window, so a tile's output has seams only
+// where it meets its neighbours.
 constexpr int kWinBytes = 36 * 1024;  // LDS for one window; 4 workgroups per CU still fit
 
 // IN_A16: `in` is 16-byte aligned (whole waves load 16-byte vectors either way).
@@ -102,45 +104,62 @@ __global__ __launch_bounds__(kThreads, OCC) void compact_kernel(const T* in, T* 
         run += readlane(incl, kWave - 1);
     }
 
-    uint32_t prefix = 0;
-    if (num_tiles > 1)
-        prefix = tile_prefix<uint32_t>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit, 0u, true);
-
-    // A prefix past n can only come from a look-back that gave up; never write past the buffer.
-    const bool fits = (int64_t)prefix + agg <= n;
-    if (!fits && threadIdx.x == 0) flag_timeout(ctrl);
-    // Phase of `out` within a 64-byte line, in elements: a window is staged so
-    // that its slot 0 lands on a line boundary (a wave's 1 KiB store then
-    // writes 16 whole lines, not parts of 17).
-    const uint32_t out_phase = (uint32_t)(((uintptr_t)out % 64) / sizeof(T));
-    for (uint32_t lo = 0; lo < agg; lo += kWin) {  // agg is the same in every wave
-        const uint32_t hi = agg - lo < kWin ? agg : lo + kWin;
-        const int64_t first = (int64_t)prefix + lo;  // output index of the window's first element
-        const uint32_t shift = (uint32_t)((first + out_phase) % kLine);
-        const uint32_t width = hi - lo;
+    // Places this thread's kept elements whose ranks lie in [lo, lo + width) at
+    // LDS index rank - lo.
+    auto stage = [&](uint32_t lo, uint32_t width) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             uint32_t t = off[k] - lo;  // window slot of the vector's first kept element; wraps below the window
 #pragma unroll
             for (int j = 0; j < V; ++j)
                 if ((keepm[(k * V + j) / 64] >> ((k * V + j) % 64)) & 1ull) {
-                    if (t < width) s_stage[t + shift] = e[k * V + j];
+                    if (t < width) s_stage[t] = e[k * V + j];
                     ++t;
                 }
         }
-        __syncthreads();
-        const uint32_t span = shift + width;  // staged slots, the shift included
-        // Output index of staged slot 0: out + dst0 is 64-byte aligned; dst0 may be
-        // below 0, and only slots from `shift` on (indices from `first`) are written.
+    };
+    // The first window (every kept element when they fit in it) is staged
+    // before the look-back: its LDS work then overlaps the wait for the prefix
+    // instead of following it while the tile is held.
+    stage(0u, agg < kWin ? agg : kWin);
+    uint32_t prefix = 0;
+    if (num_tiles > 1)
+        prefix = tile_prefix<uint32_t>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit, 0u, true);
+    else
+        __syncthreads();  // tile_prefix ends with this barrier, which the staged window needs
+
+    // A prefix past n can only come from a look-back that gave up; never write past the buffer.
+    const bool fits = (int64_t)prefix + agg <= n;
+    if (!fits && threadIdx.x == 0) flag_timeout(ctrl);
+    // Phase of `out` within a 64-byte line, in elements: each window is written
+    // from a line boundary (a wave's 1 KiB store then writes 16 whole lines, not
+    // parts of 17), reading the staged elements `shift` slots back.
+    const uint32_t out_phase = (uint32_t)(((uintptr_t)out % 64) / sizeof(T));
+    for (uint32_t lo = 0; lo < agg; lo += kWin) {  // agg is the same in every wave
+        const uint32_t hi = agg - lo < kWin ? agg : lo + kWin;
+        const uint32_t width = hi - lo;
+        if (lo > 0) {
+            stage(lo, width);
+            __syncthreads();
+        }
+        const int64_t first = (int64_t)prefix + lo;  // output index of the window's first element
+        const uint32_t shift = (uint32_t)((first + out_phase) % kLine);
+        const uint32_t span = shift + width;
+        // Output index of slot 0 of the shifted window: out + dst0 is 64-byte aligned;
+        // dst0 may be below 0, and only slots from `shift` on (indices from `first`) are written.
         const int64_t dst0 = first - (int64_t)shift;
         if (fits) {
             for (uint32_t q = threadIdx.x * V; q < span; q += kThreads * V) {
                 if (q >= shift && q + V <= span) {
-                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(s_stage + q),
-                                                reinterpret_cast<u32x4*>(out + (dst0 + q)));
+                    T v[V];
+#pragma unroll
+                    for (int j = 0; j < V; ++j) v[j] = s_stage[q - shift + j];
+                    u32x4 w;
+                    __builtin_memcpy(&w, v, kVecBytes);
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(out + (dst0 + q)));
                 } else {
                     for (uint32_t i = q; i < q + V && i < span; ++i)
-                        if (i >= shift) out[dst0 + i] = s_stage[i];
+                        if (i >= shift) out[dst0 + i] = s_stage[i - shift];
                 }
             }
         }
