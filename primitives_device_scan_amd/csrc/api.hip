@@ -560,12 +560,10 @@ int ds_radix_pass(const uint32_t* d_keys_in, uint32_t* d_keys_out, const uint32_
             if (i == 0 && j == 2) continue;  // the two inputs may share memory: both are only read
             if (ptrs[i] && ptrs[j] && overlaps(ptrs[i], bytes, ptrs[j], bytes)) return DS_ERR_OVERLAP;
         }
-    const int64_t tile = ds::sort_tile_elems(d_vals_in != nullptr);
-    const int64_t tiles = (n + tile - 1) / tile;
-    const int64_t words = ((int64_t)1 << bits) * tiles;
+    const int64_t words = ((int64_t)1 << bits) * ds::sort_table_columns(d_vals_in != nullptr, n);
     std::lock_guard<std::mutex> lock(g_mu);
     char* aux = nullptr;
-    int st = get_aux(stream, (size_t)words * 4, &aux);
+    int st = get_aux(stream, (size_t)ds::sort_aux_words(d_vals_in != nullptr, n, bits) * 4, &aux);
     if (st != DS_OK) return st;
     DevWs dws;
     Workspace* w = nullptr;

@@ -6,19 +6,27 @@
 // token dispatch" and exercise 2).
 //
 // Three launches, reduce-then-scan style:
-//   1. digit_count_kernel: each tile (kSortThreads * ITEMS keys) counts its
-//      digits in LDS and writes count[d * tiles + tile] -- a digit-major
-//      table;
+//   1. digit_count_kernel: each group of GROUP consecutive tiles (a tile is
+//      kSortThreads * ITEMS keys) counts its digits in LDS and writes
+//      count[d * groups + group] -- a digit-major table -- and, for each
+//      tile after the group's first, one tile-major row: the counts of the
+//      group's earlier tiles;
 //   2. the device-wide exclusive scan of that table (the look-back scan): the
-//      entry (d, tile) becomes the first output slot of tile's digit-d keys;
+//      entry (d, group) becomes the first output slot of the group's digit-d
+//      keys; a tile's first slot is that plus its row;
 //   3. digit_scatter_kernel: each tile ranks its keys in input order -- a
 //      wave matches equal digits with one ballot per digit bit and counts the
 //      matching lanes below each lane -- stages the tile in LDS ordered by
 //      digit, and writes each digit's run to its slot, so equal digits keep
 //      their input order (the pass is stable).
-// One tile per workgroup in both kernels: the cache line two neighbouring
-// tiles share at a bucket's run boundary is then written by both at the same
-// stage of their lives and merges in L2 instead of going to HBM twice.
+// One tile per scatter workgroup: the cache line two neighbouring tiles
+// share at a bucket's run boundary is then written by both at the same stage
+// of their lives and merges in L2 instead of going to HBM twice (a workgroup
+// that took a group's tiles in turn made the radix scatter 60% slower).
+// Groups of four in the count: its scattered table writes, one word per
+// digit and group, cost far more than their bytes (2^28 keys in one-tile
+// groups: 192 us, 4-tile groups with the rows: 183 us; the table scan
+// 14 -> 7 us).
 // For MoE alignment every scatter workgroup also derives the experts' counts
 // and block-rounded offsets from the scanned table and shifts each expert's
 // slots to its padded start (workgroup 0 writes counts, offsets and padding
@@ -47,6 +55,8 @@ constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kRadixItems = 16;                       // 8,192-key tiles
 constexpr int kRadixKvItems = 12;                     // 6,144-key tiles
 constexpr int kMoeItems = 4;                          // 2,048-id tiles
+constexpr int kRadixGroup = 4;                        // tiles per count-table entry (MoE: 1)
+constexpr int kRadixKvGroup = 4;
 constexpr int kSortMaxBuckets = 512;                  // real buckets + the spare one
 
 // digit<BITS>(k) is the same bucket as operator(), BITS = ceil(log2(buckets))
@@ -124,21 +134,29 @@ __device__ __forceinline__ int64_t xcd_contiguous_tile()
 // All of a lane's keys are loaded before any is counted: the LDS atomics
 // would otherwise keep the compiler from issuing the next load until the
 // previous one has returned, one 16-byte load in flight per lane.
-// A16: keys 16-byte aligned (whole tiles load 16-byte vectors either way).
-template <typename DIG, bool A16, int ITEMS>
+// One workgroup counts GROUP consecutive tiles (kSortThreads * ITEMS keys
+// each): table[d * groups + g] = the group's count of digit d, and for
+// GROUP > 1 pre[t * B + d] = the count of d in the tiles of t's group before
+// t, for every tile t after the first of its group. A single tile keeps one
+// histogram per wave; a group keeps one per tile, shared by the waves.
+// A16: keys 16-byte aligned (whole groups load 16-byte vectors either way).
+template <typename DIG, bool A16, int ITEMS, int GROUP>
 __global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                                  DIG dig, uint32_t* __restrict__ table,
+                                                                 uint32_t* __restrict__ pre, int64_t groups,
                                                                  int64_t tiles)
 {
     static_assert(ITEMS % 4 == 0, "whole 16-byte vectors per lane");
-    constexpr int kTile = kSortThreads * ITEMS, kVecs = ITEMS / 4;
-    __shared__ uint32_t hist[kSortWaves][kSortMaxBuckets];
+    constexpr int kTile = kSortThreads * ITEMS, kPer = ITEMS * GROUP, kVecs = kPer / 4, kTileVecs = ITEMS / 4;
+    constexpr int kSets = GROUP == 1 ? kSortWaves : 1;
+    __shared__ uint32_t hist[GROUP][kSets][kSortMaxBuckets];
     const uint32_t B = dig.buckets;
-    const int wave = (int)(threadIdx.x / kWave);
-    for (uint32_t i = threadIdx.x; i < kSortWaves * kSortMaxBuckets; i += kSortThreads) (&hist[0][0])[i] = 0;
-    const int64_t tile = xcd_contiguous_tile();
-    const int64_t base = tile * kTile;
-    if (base + kTile <= n) {
+    const int set = GROUP == 1 ? (int)(threadIdx.x / kWave) : 0;
+    for (uint32_t i = threadIdx.x; i < GROUP * kSets * kSortMaxBuckets; i += kSortThreads) (&hist[0][0][0])[i] = 0;
+    const int64_t g = xcd_contiguous_tile();
+    const int64_t base = g * ((int64_t)kTile * GROUP);
+    if (base + (int64_t)kTile * GROUP <= n) {
+        // vector v of a lane lies in tile v / kTileVecs of the group
         using V = typename VecOf<A16>::type;
         const V* p = reinterpret_cast<const V*>(keys + base) + threadIdx.x;
         V k[kVecs];
@@ -150,30 +168,36 @@ __global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t d = dig(k[v][j]);
-                if (!DIG::kSpareKeys || d < B) atomicAdd(&hist[wave][d], 1u);
+                if (!DIG::kSpareKeys || d < B) atomicAdd(&hist[v / kTileVecs][set][d], 1u);
             }
     } else {
-        // the ragged last tile: element by element, guarded
-        uint32_t k[ITEMS];
+        // the ragged last group, element by element: key i of a lane lies in tile i / ITEMS
+        uint32_t k[kPer];
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
+        for (int i = 0; i < kPer; ++i) {
             const int64_t at = base + threadIdx.x + (int64_t)i * kSortThreads;
             k[i] = at < n ? keys[at] : 0u;
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
+        for (int i = 0; i < kPer; ++i) {
             const int64_t at = base + threadIdx.x + (int64_t)i * kSortThreads;
             const uint32_t d = dig(k[i]);
-            if (at < n && d < B) atomicAdd(&hist[wave][d], 1u);
+            if (at < n && d < B) atomicAdd(&hist[i / ITEMS][set][d], 1u);
         }
     }
     __syncthreads();
     for (uint32_t d = threadIdx.x; d < B; d += kSortThreads) {
-        uint32_t c = 0;
+        uint32_t run = 0;
 #pragma unroll
-        for (int w = 0; w < kSortWaves; ++w) c += hist[w][d];
-        table[(int64_t)d * tiles + tile] = c;
+        for (int i = 0; i < GROUP; ++i) {
+            if (i > 0 && g * GROUP + i < tiles) pre[(g * GROUP + i) * B + d] = run;
+            uint32_t c = 0;
+#pragma unroll
+            for (int w = 0; w < kSets; ++w) c += hist[i][w][d];
+            run += c;
+        }
+        table[(int64_t)d * groups + g] = run;
     }
 }
 
@@ -333,6 +357,26 @@ __device__ __forceinline__ void write_runs(const SortLds<VALS, ITEMS>& sh, uint3
 {
     const uint32_t B = dig.buckets;
     const uint32_t real = sh.s_real;
+    if constexpr (VALS == 0) {
+        if (real == kSortThreads * ITEMS && out_cap > 0) {
+            // A whole tile of keys, all in real buckets: each thread takes
+            // ITEMS of them with every LDS read issued up front, where the
+            // loop below waits on two dependent reads per key. (Keys only:
+            // with values the same form was 7% slower at 2^28 pairs.)
+            uint32_t k[ITEMS], pos[ITEMS];
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) k[i] = sh.stage_k[threadIdx.x + i * kSortThreads];
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i)
+                pos[i] = sh.gdelta[dig.template digit<BITS>(k[i])] + threadIdx.x + (uint32_t)(i * kSortThreads);
+            // pos < out_cap as a 32-bit compare (pos is 32-bit)
+            const uint32_t last = out_cap > (int64_t)0xFFFFFFFFu ? 0xFFFFFFFFu : (uint32_t)(out_cap - 1);
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i)
+                if (pos[i] <= last) keys_out[pos[i]] = k[i];
+            return;
+        }
+    }
     for (uint32_t j = threadIdx.x; j < real; j += kSortThreads) {
         const uint32_t k = sh.stage_k[j];
         const uint32_t d = dig.template digit<BITS>(k);
@@ -382,12 +426,17 @@ __device__ __forceinline__ void moe_bases(uint32_t* gbase, uint32_t* s_wave, con
     }
 }
 
-template <typename DIG, int VALS, int BITS, int ITEMS>
+// One tile per workgroup (neighbouring tiles, which share a cache line at
+// each bucket's run boundary, are then written at the same time). Its first
+// slot for bucket d is its group's entry of the scanned table plus, after
+// the group's first tile, its row of the group prefixes.
+template <typename DIG, int VALS, int BITS, int ITEMS, int GROUP>
 __global__ __launch_bounds__(kSortThreads) void digit_scatter_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, int64_t n, DIG dig, const uint32_t* __restrict__ slots, MoeSlots moe,
-    int64_t tiles, int64_t out_cap)
+    uint32_t* __restrict__ vals_out, int64_t n, DIG dig, const uint32_t* __restrict__ slots,
+    const uint32_t* __restrict__ pre, MoeSlots moe, int64_t groups, int64_t out_cap)
 {
+    static_assert(GROUP == 1 || VALS != 2, "MoE offsets are read per tile");
     __shared__ SortLds<VALS, ITEMS> sh;
     const int64_t tile = xcd_contiguous_tile();
     const int64_t first = tile * (int64_t)(kSortThreads * ITEMS);
@@ -397,9 +446,12 @@ __global__ __launch_bounds__(kSortThreads) void digit_scatter_kernel(
     uint32_t key[ITEMS], val[ITEMS];
     const bool whole = load_tile<VALS, ITEMS>(keys, vals_in, n, first, key, val);
     if (moe.hist) {
-        moe_bases(sh.gbase, sh.s_wave, slots, tiles, tile, dig.buckets, moe, n);
+        moe_bases(sh.gbase, sh.s_wave, slots, groups, tile, dig.buckets, moe, n);
     } else {
-        for (uint32_t d = threadIdx.x; d < dig.buckets; d += kSortThreads) sh.gbase[d] = slots[(int64_t)d * tiles + tile];
+        const int64_t g = tile / GROUP;
+        const bool later = GROUP > 1 && tile % GROUP != 0;
+        for (uint32_t d = threadIdx.x; d < dig.buckets; d += kSortThreads)
+            sh.gbase[d] = slots[(int64_t)d * groups + g] + (later ? pre[tile * dig.buckets + d] : 0u);
     }
     __syncthreads();
     rank_and_stage<DIG, VALS, BITS, ITEMS>(sh, key, val, whole, n, dig, first);
@@ -501,27 +553,32 @@ __global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(co
     }
 }
 
-template <typename DIG, int VALS, int ITEMS>
+// GROUP: tiles per entry of the count table. For a radix pass hist and slots
+// are the same buffer (scanned in place) and pre follows the table in it.
+template <typename DIG, int VALS, int ITEMS, int GROUP>
 static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out,
                                       uint32_t* vals_out, int64_t n, DIG dig, uint32_t* hist, uint32_t* slots,
-                                      const MoeSlots& moe, int64_t out_cap, const DevWs& ws, uint32_t spin_limit,
-                                      hipStream_t st)
+                                      uint32_t* pre, const MoeSlots& moe, int64_t out_cap, const DevWs& ws,
+                                      uint32_t spin_limit, hipStream_t st)
 {
-    const int tile_elems = kSortThreads * ITEMS;
-    const int64_t tiles = (n + tile_elems - 1) / tile_elems;
-    const dim3 grid((unsigned)tiles), block(kSortThreads);
+    const int64_t tile_elems = (int64_t)kSortThreads * ITEMS;
+    const int64_t tiles = (n + tile_elems - 1) / tile_elems, groups = (tiles + GROUP - 1) / GROUP;
+    if (GROUP > 1 && !pre) return hipErrorInvalidValue;
+    const dim3 block(kSortThreads);
     if (aligned16(keys))
-        digit_count_kernel<DIG, true, ITEMS><<<grid, block, 0, st>>>(keys, n, dig, hist, tiles);
+        digit_count_kernel<DIG, true, ITEMS, GROUP><<<dim3((unsigned)groups), block, 0, st>>>(keys, n, dig, hist, pre,
+                                                                                           groups, tiles);
     else
-        digit_count_kernel<DIG, false, ITEMS><<<grid, block, 0, st>>>(keys, n, dig, hist, tiles);
+        digit_count_kernel<DIG, false, ITEMS, GROUP><<<dim3((unsigned)groups), block, 0, st>>>(keys, n, dig, hist, pre,
+                                                                                            groups, tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_lookback_scan(kU32, false, hist, slots, (int64_t)dig.buckets * tiles, ws, spin_limit, st);
+    e = launch_lookback_scan(kU32, false, hist, slots, (int64_t)dig.buckets * groups, ws, spin_limit, st);
     if (e != hipSuccess) return e;
     const int bits = dig.buckets > 1 ? 32 - __builtin_clz(dig.buckets - 1) : 0;
 #define DS_SCATTER(BITS)                                                                                      \
-    digit_scatter_kernel<DIG, VALS, BITS, ITEMS><<<grid, block, 0, st>>>(keys, vals_in, keys_out, vals_out, n, dig,         \
-                                                                  slots, moe, tiles, out_cap);                \
+    digit_scatter_kernel<DIG, VALS, BITS, ITEMS, GROUP><<<dim3((unsigned)tiles), block, 0, st>>>(             \
+        keys, vals_in, keys_out, vals_out, n, dig, slots, pre, moe, groups, out_cap);                         \
     break
     switch (bits) {
     case 0: DS_SCATTER(0);
@@ -543,6 +600,16 @@ static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals
 
 int64_t moe_one_launch_max() { return kMoeOneLaunchMax; }
 int64_t sort_tile_elems(bool values) { return (int64_t)kSortThreads * (values ? kRadixKvItems : kRadixItems); }
+static int64_t sort_tiles(bool values, int64_t n) { return (n + sort_tile_elems(values) - 1) / sort_tile_elems(values); }
+int64_t sort_table_columns(bool values, int64_t n)
+{
+    const int64_t group = values ? kRadixKvGroup : kRadixGroup;
+    return (sort_tiles(values, n) + group - 1) / group;
+}
+int64_t sort_aux_words(bool values, int64_t n, int bits)
+{
+    return ((int64_t)1 << bits) * (sort_table_columns(values, n) + sort_tiles(values, n));
+}
 int64_t moe_tile_elems() { return (int64_t)kSortThreads * kMoeItems; }
 int sort_max_buckets() { return kSortMaxBuckets - 1; }
 
@@ -554,11 +621,14 @@ hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint
     if (!table) return hipErrorInvalidValue;
     const RadixDigit dig{(uint32_t)shift, (1u << bits) - 1u, 1u << bits};
     const MoeSlots none{nullptr, 0, nullptr, nullptr, nullptr};
+    // the table (buckets x groups, scanned in place), then the group prefixes (buckets x tiles)
+    uint32_t* pre = table + (int64_t)dig.buckets * sort_table_columns(vals_in != nullptr, n);
     if (vals_in)
-        return counting_sort_typed<RadixDigit, 1, kRadixKvItems>(keys, vals_in, keys_out, vals_out, n, dig, table, table, none, n, ws,
-                                                  spin_limit, stream);
-    return counting_sort_typed<RadixDigit, 0, kRadixItems>(keys, nullptr, keys_out, nullptr, n, dig, table, table, none, n, ws,
-                                              spin_limit, stream);
+        return counting_sort_typed<RadixDigit, 1, kRadixKvItems, kRadixKvGroup>(keys, vals_in, keys_out, vals_out, n, dig,
+                                                                              table, table, pre, none, n, ws, spin_limit,
+                                                                              stream);
+    return counting_sort_typed<RadixDigit, 0, kRadixItems, kRadixGroup>(keys, nullptr, keys_out, nullptr, n, dig, table,
+                                                                      table, pre, none, n, ws, spin_limit, stream);
 }
 
 hipError_t launch_moe_align(const int32_t* ids, int64_t n, int experts, const MoeOut& out, uint32_t* hist,
@@ -589,8 +659,9 @@ hipError_t launch_moe_align(const int32_t* ids, int64_t n, int experts, const Mo
         return hipGetLastError();
     }
     const MoeSlots moe{hist, out.block, out.counts, out.offsets, out.sorted};
-    return counting_sort_typed<ExpertDigit, 2, kMoeItems>((const uint32_t*)ids, nullptr, nullptr, (uint32_t*)out.sorted, n, dig,
-                                               hist, slots, moe, out.capacity, ws, spin_limit, stream);
+    return counting_sort_typed<ExpertDigit, 2, kMoeItems, 1>((const uint32_t*)ids, nullptr, nullptr, (uint32_t*)out.sorted,
+                                                             n, dig, hist, slots, nullptr, moe, out.capacity, ws,
+                                                             spin_limit, stream);
 }
 
 }  // namespace ds

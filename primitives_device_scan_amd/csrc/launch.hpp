@@ -61,6 +61,8 @@ hipError_t launch_pattern(int mode, int vpt, int layout, const void* in, void* o
 // tile, and the most real buckets a pass can have.
 int64_t moe_one_launch_max();          // MoE inputs up to this many ids take one single-workgroup launch
 int64_t sort_tile_elems(bool values);  // radix pass, keys only or with values
+int64_t sort_table_columns(bool values, int64_t n);  // radix pass: entries per digit in its count table
+int64_t sort_aux_words(bool values, int64_t n, int bits);  // radix pass: its table and group prefixes
 int64_t moe_tile_elems();              // MoE alignment
 int sort_max_buckets();
 

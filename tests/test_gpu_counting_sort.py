@@ -60,7 +60,9 @@ DIGITS = [(0, 8), (8, 8), (24, 8), (28, 4), (31, 1), (5, 3)]
 
 
 def around_tiles(T: int):
-    return (1, 7, 64, 4095, 4096, 4097, T - 1, T, T + 1, 3 * T + 5, 70 * T + 3)
+    # also around groups of 2 and 4 tiles (a workgroup may take several tiles in turn)
+    return (1, 7, 64, 4095, 4096, 4097, T - 1, T, T + 1, 2 * T, 3 * T + 5, 4 * T - 1, 4 * T, 4 * T + 1, 8 * T + 5,
+            9 * T, 70 * T + 3)
 
 
 @pytest.mark.parametrize("shift,bits", DIGITS)
