@@ -565,8 +565,8 @@ def main():
     }
 
     # Same-pattern copy: the practical ceiling (in -> out, 800 MB moved).
-    def timed(fn, reps=20):
-        for _ in range(3):
+    def timed(fn, reps=20, warm=3):
+        for _ in range(warm):
             fn()
         es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         torch.cuda.synchronize()
@@ -710,13 +710,17 @@ def main():
         keys = torch.from_numpy(datagen.workload("compact_256m").view(np.int32)).to(dev)
         vals = torch.from_numpy(datagen.keys_u32(8, nk).view(np.int32)).to(dev)
         kout, vout = torch.empty_like(keys), torch.empty_like(vals)
+        # The scatter is bound by VALU issue, so its time follows the clock,
+        # which dips for a few ms once back-to-back passes start (470 -> 650 ->
+        # 500 us per scatter over the first 15 ms in a kernel trace): each leg
+        # is timed after 20 untimed passes.
         for shift in (0, 24):
             r_ms = timed(lambda: L.ds_radix_pass(keys.data_ptr(), kout.data_ptr(), None, None, nk, shift, 8, sh),
-                         reps=10)
+                         reps=20, warm=20)
             extras[f"radix_pass_256m_shift{shift}_us"] = round(r_ms * 1e3, 1)
             extras[f"radix_pass_256m_shift{shift}_alg_gbs"] = round(12 * nk / (r_ms * 1e-3) / 1e9, 1)
         rv_ms = timed(lambda: L.ds_radix_pass(keys.data_ptr(), kout.data_ptr(), vals.data_ptr(), vout.data_ptr(), nk,
-                                              0, 8, sh), reps=10)
+                                              0, 8, sh), reps=20, warm=20)
         extras["radix_pass_kv_256m_us"] = round(rv_ms * 1e3, 1)
         extras["radix_pass_kv_256m_alg_gbs"] = round(20 * nk / (rv_ms * 1e-3) / 1e9, 1)
         del keys, vals, kout, vout
