@@ -202,10 +202,19 @@ def test_moe_shapes(experts, top_k, block):
 
 @pytest.mark.parametrize("n", [4095, 4096, 4097, 8191, 8192, 8193, 12289])
 def test_moe_one_launch_boundary(n):
-    # up to 8,192 ids one single-workgroup launch aligns everything; above, the four-launch pipeline
+    # up to 8,192 ids one single-workgroup launch aligns everything; above, three launches
     ids = datagen.moe_topk_ids(n, n, 1, 100).ravel().copy()
     ids[::13] = -3
     check_moe(ids, 100, 16, f"n={n}")
+
+
+def test_moe_large():
+    # about a million ids (512 tiles and beyond), an eighth of them dropped
+    T = sort_tile("moe_align")
+    for n in (512 * T - 5, 512 * T, 512 * T + 1, 600 * T + 3):
+        ids = (datagen.keys_u32(n, n) % 257).astype(np.int32)  # 256: dropped
+        say("moe", n, "ids")
+        check_moe(ids, 256, 64, f"n={n}")
 
 
 def test_moe_dropped_ids_and_empty():
