@@ -23,10 +23,10 @@
 // share at a bucket's run boundary is then written by both at the same stage
 // of their lives and merges in L2 instead of going to HBM twice (a workgroup
 // that took a group's tiles in turn made the radix scatter 60% slower).
-// Groups of four in the count: its scattered table writes, one word per
-// digit and group, cost far more than their bytes (2^28 keys in one-tile
-// groups: 192 us, 4-tile groups with the rows: 183 us; the table scan
-// 14 -> 7 us).
+// Groups of four in the count: its table writes cost far more than their
+// bytes, the scattered ones most (2^28 keys in one-tile groups: 192 us;
+// 4-tile groups with 32-bit rows: 183 us, with 16-bit rows 13 us less per
+// pass; the table scan 14 -> 7 us).
 // For MoE alignment every scatter workgroup also derives the experts' counts
 // and block-rounded offsets from the scanned table and shifts each expert's
 // slots to its padded start (workgroup 0 writes counts, offsets and padding
@@ -136,17 +136,18 @@ __device__ __forceinline__ int64_t xcd_contiguous_tile()
 // previous one has returned, one 16-byte load in flight per lane.
 // One workgroup counts GROUP consecutive tiles (kSortThreads * ITEMS keys
 // each): table[d * groups + g] = the group's count of digit d, and for
-// GROUP > 1 pre[t * B + d] = the count of d in the tiles of t's group before
+// GROUP > 1 pre[t * B + d] (16 bits) = the count of d in the tiles of t's group before
 // t, for every tile t after the first of its group. A single tile keeps one
 // histogram per wave; a group keeps one per tile, shared by the waves.
 // A16: keys 16-byte aligned (whole groups load 16-byte vectors either way).
 template <typename DIG, bool A16, int ITEMS, int GROUP>
 __global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                                  DIG dig, uint32_t* __restrict__ table,
-                                                                 uint32_t* __restrict__ pre, int64_t groups,
+                                                                 uint16_t* __restrict__ pre, int64_t groups,
                                                                  int64_t tiles)
 {
     static_assert(ITEMS % 4 == 0, "whole 16-byte vectors per lane");
+    static_assert((GROUP - 1) * kSortThreads * ITEMS <= 0xFFFF, "a prefix row entry fits 16 bits");
     constexpr int kTile = kSortThreads * ITEMS, kPer = ITEMS * GROUP, kVecs = kPer / 4, kTileVecs = ITEMS / 4;
     constexpr int kSets = GROUP == 1 ? kSortWaves : 1;
     __shared__ uint32_t hist[GROUP][kSets][kSortMaxBuckets];
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kSortThreads) void digit_count_kernel(const uint32_
         uint32_t run = 0;
 #pragma unroll
         for (int i = 0; i < GROUP; ++i) {
-            if (i > 0 && g * GROUP + i < tiles) pre[(g * GROUP + i) * B + d] = run;
+            if (i > 0 && g * GROUP + i < tiles) pre[(g * GROUP + i) * B + d] = (uint16_t)run;
             uint32_t c = 0;
 #pragma unroll
             for (int w = 0; w < kSets; ++w) c += hist[i][w][d];
@@ -434,7 +435,7 @@ template <typename DIG, int VALS, int BITS, int ITEMS, int GROUP>
 __global__ __launch_bounds__(kSortThreads) void digit_scatter_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, int64_t n, DIG dig, const uint32_t* __restrict__ slots,
-    const uint32_t* __restrict__ pre, MoeSlots moe, int64_t groups, int64_t out_cap)
+    const uint16_t* __restrict__ pre, MoeSlots moe, int64_t groups, int64_t out_cap)
 {
     static_assert(GROUP == 1 || VALS != 2, "MoE offsets are read per tile");
     __shared__ SortLds<VALS, ITEMS> sh;
@@ -558,7 +559,7 @@ __global__ __launch_bounds__(kMoeThreadsOne) void moe_align_one_launch_kernel(co
 template <typename DIG, int VALS, int ITEMS, int GROUP>
 static hipError_t counting_sort_typed(const uint32_t* keys, const uint32_t* vals_in, uint32_t* keys_out,
                                       uint32_t* vals_out, int64_t n, DIG dig, uint32_t* hist, uint32_t* slots,
-                                      uint32_t* pre, const MoeSlots& moe, int64_t out_cap, const DevWs& ws,
+                                      uint16_t* pre, const MoeSlots& moe, int64_t out_cap, const DevWs& ws,
                                       uint32_t spin_limit, hipStream_t st)
 {
     const int64_t tile_elems = (int64_t)kSortThreads * ITEMS;
@@ -622,7 +623,7 @@ hipError_t launch_radix_pass(const uint32_t* keys, const uint32_t* vals_in, uint
     const RadixDigit dig{(uint32_t)shift, (1u << bits) - 1u, 1u << bits};
     const MoeSlots none{nullptr, 0, nullptr, nullptr, nullptr};
     // the table (buckets x groups, scanned in place), then the group prefixes (buckets x tiles)
-    uint32_t* pre = table + (int64_t)dig.buckets * sort_table_columns(vals_in != nullptr, n);
+    uint16_t* pre = reinterpret_cast<uint16_t*>(table + (int64_t)dig.buckets * sort_table_columns(vals_in != nullptr, n));
     if (vals_in)
         return counting_sort_typed<RadixDigit, 1, kRadixKvItems, kRadixKvGroup>(keys, vals_in, keys_out, vals_out, n, dig,
                                                                               table, table, pre, none, n, ws, spin_limit,
