@@ -173,6 +173,32 @@ __device__ __forceinline__ void store_vec(T* __restrict__ out, int64_t seg, int 
     }
 }
 
+// e + head, stored vector by vector: each vector's additions, then its
+// store. After each store an empty asm with a memory clobber claims to
+// touch the next vector's values, so the compiler can neither hoist the
+// later additions above the store nor sink the store below them: the first
+// store leaves after one vector's additions instead of the whole tile's.
+template <typename T, int VPT, bool A16 = true>
+__device__ __forceinline__ void add_store_vec(T* __restrict__ out, int64_t seg, int lane,
+                                              T (&e)[Shape<T, VPT>::kItems], T head)
+{
+    using V = typename VecOf<A16>::type;
+    constexpr int PV = Shape<T, VPT>::kPerVec;
+    V* p = reinterpret_cast<V*>(out + seg) + lane;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+#pragma unroll
+        for (int j = 0; j < PV; ++j) e[k * PV + j] = head + e[k * PV + j];
+        V r;
+        __builtin_memcpy(&r, &e[k * PV], kVecBytes);
+        __builtin_nontemporal_store(r, p + k * kWave);
+        if (k + 1 < VPT) {
+#pragma unroll
+            for (int j = 0; j < PV; ++j) asm volatile("" : "+v"(e[(k + 1) * PV + j])::"memory");
+        }
+    }
+}
+
 template <typename T, int VPT>
 __device__ __forceinline__ void store_scalar(T* __restrict__ out, int64_t seg, int64_t n, int lane,
                                              const T (&e)[Shape<T, VPT>::kItems])
