@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads, (ScanOcc<T, VPT>::value)) void lookback_s
     // the wait below, into the prefix add (v_add3); done after the prefix
     // arrives, they delay the stores: int32 at n = 100M took 140.0-140.6 us
     // cold that way against 136.8-138.0 us pinned. The 8-byte exclusive tile
-    // (144 KiB) spills 28 bytes per lane when pinned and is left as it is.
+    // fills 255 VGPRs and is left as it is.
     if constexpr (sizeof(T) == 4 || INCLUSIVE) pin_in_registers(e);
     const T prefix =
         num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit, first, true) : first;
@@ -59,8 +59,9 @@ __global__ __launch_bounds__(kThreads, (ScanOcc<T, VPT>::value)) void lookback_s
     // stores begin after one vector's additions rather than all of them: the
     // tile is held that much less (n = 100M cold: int32 138.7-140.5 ->
     // 133.2-134.8 us, fp32 135.9-136.7 -> 133.3-134.4, int64 inclusive
-    // 143.0-144.1 -> 140.8-142.3). The 8-byte exclusive tile would spill.
-    if (whole && (sizeof(T) == 4 || INCLUSIVE)) {
+    // 143.0-144.1 -> 140.8-142.3; int64 exclusive at n = 50M, with 128 KiB
+    // tiles in place of 144 KiB, 141.3-143.2 -> 136.3-139.1).
+    if (whole) {
         add_store_vec<T, VPT, A16>(out, seg, lane, e, prefix + wave_excl);
     } else {
         add_uniform(e, prefix + wave_excl);
