@@ -19,16 +19,16 @@ namespace ds {
 //    80 KiB tiles at 3 per CU, the earlier choice; 112 and 144 KiB tiles took
 //    141-143 us, and 112 KiB at 3 per CU spills. A held copy shows the same
 //    order: 135 us at 128 KiB and 2 per CU, 143-144 us at 80-112 KiB and 3-4.
-//    8-byte types: 128 / 112 KiB tiles (exclusive / inclusive) at 2 per CU
-//    (ScanOcc); 96-112 KiB at 3 per CU spill and were slower. With the prefix
-//    added and stored one vector at a time, the 128 KiB exclusive tile (255
-//    VGPRs, no spill) took 136-139 us at n = 50M after a cache eviction,
-//    against 141-143 us for 144 KiB tiles that add the prefix first;
+//    8-byte types take the same 128 KiB tile (16,384 elements, 166 VGPRs, no
+//    spill) at 2 per CU (ScanOcc); 96-112 KiB at 3 per CU spill and were
+//    slower. With the prefix added and stored one vector at a time, n = 50M
+//    after a cache eviction: exclusive 136-139 us against 141-143 us for the
+//    earlier 144 KiB tile, inclusive 137-138 us against 141-143 us at 112 KiB;
 //  - three-pass scan and compaction: 64 KiB tiles (the three-pass scan has no
 //    wait to hide; compaction's keep mask holds 64 elements).
 template <typename T, bool INCLUSIVE>
 struct ScanVPT {
-    static constexpr int value = sizeof(T) == 8 ? (INCLUSIVE ? 28 : 32) : 32;
+    static constexpr int value = 32;
 };
 // Workgroups per CU the look-back kernel is compiled for (waves per SIMD):
 // tiles past 80 KiB need up to 256 VGPRs; every other tile fits 3.

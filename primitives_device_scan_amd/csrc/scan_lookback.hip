@@ -50,17 +50,18 @@ __global__ __launch_bounds__(kThreads, (ScanOcc<T, VPT>::value)) void lookback_s
     // Left to itself the compiler sinks the integer scan's last additions past
     // the wait below, into the prefix add (v_add3); done after the prefix
     // arrives, they delay the stores: int32 at n = 100M took 140.0-140.6 us
-    // cold that way against 136.8-138.0 us pinned. The 8-byte exclusive tile
-    // fills 255 VGPRs and is left as it is.
-    if constexpr (sizeof(T) == 4 || INCLUSIVE) pin_in_registers(e);
+    // cold that way against 136.8-138.0 us pinned. (The 8-byte exclusive tile
+    // takes the same time pinned, in 166 VGPRs rather than 255.)
+    pin_in_registers(e);
     const T prefix =
         num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit, first, true) : first;
     // The prefix is added and each vector stored in turn, so the tile's
     // stores begin after one vector's additions rather than all of them: the
     // tile is held that much less (n = 100M cold: int32 138.7-140.5 ->
     // 133.2-134.8 us, fp32 135.9-136.7 -> 133.3-134.4, int64 inclusive
-    // 143.0-144.1 -> 140.8-142.3; int64 exclusive at n = 50M, with 128 KiB
-    // tiles in place of 144 KiB, 141.3-143.2 -> 136.3-139.1).
+    // 143.0-144.1 -> 140.8-142.3; with 128 KiB int64 tiles in place of 144
+    // and 112 KiB at n = 50M, exclusive 141.3-143.2 -> 136.3-139.1 and
+    // inclusive 140.6-142.5 -> 136.9-137.9).
     if (whole) {
         add_store_vec<T, VPT, A16>(out, seg, lane, e, prefix + wave_excl);
     } else {
