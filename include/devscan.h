@@ -157,8 +157,8 @@ int ds_scan_seeded(int dtype, int inclusive, const void* d_in, void* d_out, int6
  * capture, tight serving loops, harnesses that forbid hipMalloc. It calls no
  * allocating routine: its control block and status words live in a fixed
  * 4 MiB array in the library's own device memory, one per GPU, held until the
- * process ends, with room for 32,766 tiles (n up to 1.07G 4-byte and at least
- * 469M 8-byte elements; DS_ERR_TOO_LARGE beyond). Every call on a GPU shares
+ * process ends, with room for 32,766 tiles (n up to 1.07G 4-byte and 537M
+ * 8-byte elements; DS_ERR_TOO_LARGE beyond). Every call on a GPU shares
  * that GPU's array, so calls that overlap in time on one GPU (different
  * streams, no ordering between them) race and give wrong results; order them
  * on one stream. The first call on a device enqueues a kernel that clears
@@ -212,16 +212,17 @@ int ds_compact_unordered(int dtype, const void* d_in, void* d_out, int64_t* d_nu
  * parallel patterns", opening paragraph): d_keys_out holds the n uint32 keys
  * ordered by the digit (key >> shift) & (2^bits - 1), keys with equal digits
  * in input order. d_vals_in / d_vals_out (both NULL, or both n uint32
- * values) carry a value with each key. Three launches: per-tile digit counts
- * into a digit-major table, the device-wide exclusive scan of that table,
- * then a stable scatter. Four-byte aligned device pointers; an output may
+ * values) carry a value with each key. Three launches: digit counts per
+ * group of four tiles into a digit-major table (with each later tile's counts
+ * within its group), the device-wide exclusive scan of that table, then a
+ * stable scatter. Four-byte aligned device pointers; an output may
  * not overlap any other buffer (DS_ERR_OVERLAP), the two inputs may share
  * memory. 1 <= bits <= 8, 0 <= shift,
  * shift + bits <= 32 (else DS_ERR_INVALID_VALUE); n < 2^32 (else
- * DS_ERR_TOO_LARGE). Scratch: 2^bits x (number of tiles) words, a tile being
- * ds_tile_elems(DS_UINT32, DS_TILE_OF_COUNTING_SORT) keys, or
- * DS_TILE_OF_COUNTING_SORT_VALUES with values; cached per (device, stream)
- * like the scan workspace.
+ * DS_ERR_TOO_LARGE). Scratch: 2^bits x (groups + tiles) 32-bit words, a
+ * tile being ds_tile_elems(DS_UINT32, DS_TILE_OF_COUNTING_SORT) keys, or
+ * DS_TILE_OF_COUNTING_SORT_VALUES with values, and a group four tiles; cached
+ * per (device, stream) like the scan workspace.
  */
 int ds_radix_pass(const uint32_t* d_keys_in, uint32_t* d_keys_out, const uint32_t* d_vals_in,
                   uint32_t* d_vals_out, int64_t n, int shift, int bits, hipStream_t stream);
