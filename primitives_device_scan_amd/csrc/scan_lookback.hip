@@ -56,27 +56,23 @@ __global__ __launch_bounds__(kThreads, (ScanOcc<T, VPT>::value)) void lookback_s
     const T prefix =
         num_tiles > 1 ? tile_prefix<T>(tile, num_tiles, epoch, agg, ctrl, status, spin_limit, first, true) : first;
     // The prefix is added and each vector stored in turn, so the tile's
-    // stores begin after one vector's additions rather than all of them: the
-    // tile is held that much less (n = 100M cold: int32 138.7-140.5 ->
-    // 133.2-134.8 us, fp32 135.9-136.7 -> 133.3-134.4, int64 inclusive
-    // 143.0-144.1 -> 140.8-142.3; with 128 KiB int64 tiles in place of 144
-    // and 112 KiB at n = 50M, exclusive 141.3-143.2 -> 136.3-139.1 and
-    // inclusive 140.6-142.5 -> 136.9-137.9).
+    // stores begin after one vector's additions rather than all of them and
+    // the tile is held that much less. Cold, 800 MB of input: int32 (n = 100M)
+    // 138.7-140.5 -> 133.2-134.8 us, fp32 135.9-136.7 -> 133.3-134.4; int64
+    // (n = 50M, with 128 KiB tiles in place of 144 / 112 KiB) exclusive
+    // 141.3-143.2 -> 136.3-139.1, inclusive 140.6-142.5 -> 136.9-137.9.
     if (whole) {
         add_store_vec<T, VPT, A16>(out, seg, lane, e, prefix + wave_excl);
     } else {
         add_uniform(e, prefix + wave_excl);
-        if (whole)
-            store_vec<T, VPT, A16>(out, seg, lane, e);
-        else
-            store_scalar<T, VPT>(out, seg, n, lane, e);
+        store_scalar<T, VPT>(out, seg, n, lane, e);
     }
     if (threadIdx.x == 0) keep_alive(touched);
 }
 
 // Vectors per thread for n elements: the per-type large tile (ScanVPT) from
 // 64 MiB of data on, where resident bytes must hide the look-back; below, a
-// large tile would leave most CUs idle (1M int32 fill 35 workgroups of 112 KiB)
+// large tile would leave most CUs idle (1M int32 fill 31 workgroups of 128 KiB)
 // and a small last tile costs element-wise loads, so inputs up to 8 MiB take
 // 8 vectors per thread, up to 32 MiB 12 and up to 64 MiB 16 (measured: one
 // 4,096-int32 tile 7.9 -> 3.8 us, 1M int32 10.0 -> 5.6 us, 8M int32 14.5 ->

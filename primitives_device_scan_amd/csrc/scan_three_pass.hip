@@ -83,14 +83,18 @@ __global__ __launch_bounds__(kThreads) void tile_rescan_kernel(const T* in, T* o
         load_vec<T, kThreePassVPT, A16>(in, seg, lane, e);
     else
         load_scalar<T, kThreePassVPT>(in, seg, n, lane, e, T(0));
-    T off[kThreePassVPT];
+    // The sums of the waves before this one come from a reduction first, so
+    // each vector can be stored as soon as it is scanned.
     T wave_excl;
-    tile_local_scan<T, V, kThreePassVPT>(e, off, wave_excl, s_wave);
-    tile_finish<T, V, kThreePassVPT, INCLUSIVE>(e, off, wave_excl, offsets[tile]);
-    if (whole)
-        store_vec<T, kThreePassVPT, A16>(out, seg, lane, e);
-    else
+    (void)tile_reduce<T, S::kItems>(e, wave_excl, s_wave);
+    const T head = offsets[tile] + wave_excl;
+    if (whole) {
+        scan_store_vec<T, V, kThreePassVPT, INCLUSIVE, A16>(out, seg, lane, e, head);
+    } else {
+        scan_in_wave<T, V, kThreePassVPT, INCLUSIVE>(e);
+        add_uniform(e, head);
         store_scalar<T, kThreePassVPT>(out, seg, n, lane, e);
+    }
 }
 
 template <typename T, bool A16>

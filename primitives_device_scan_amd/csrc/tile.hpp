@@ -214,51 +214,12 @@ __device__ __forceinline__ void store_scalar(T* __restrict__ out, int64_t seg, i
 }
 
 // ---------------------------------------------------------------------------
-// Scan of one tile held in registers, up to the tile's own offsets.
-//
-// V is the number of elements per 16-byte vector of the data (4 or 2); T is
-// the type being summed (the data, or 32-bit keep counts in compaction).
-// In: e = the thread's values. Out: e = inclusive prefix inside each vector
-// (the serial scan of the thread's chunk), off[k] = sum of everything in the
-// wave before vector k of this lane, wave_excl = sum of the waves before this
-// one, return value = the tile aggregate. s_wave is kWaves values of LDS.
-// Contains one workgroup barrier.
+// Scan of one tile held in registers. V is the number of elements per 16-byte
+// vector of the data (4 or 2); T is the type being summed (the data, or 32-bit
+// keep counts in compaction). tile_reduce gives the tile aggregate and the
+// sums of the waves before each wave; scan_in_wave (or scan_store_vec, which
+// also stores) scans each wave's segment.
 // ---------------------------------------------------------------------------
-template <typename T, int V, int VPT>
-__device__ __forceinline__ T tile_local_scan(T (&e)[V * VPT], T (&off)[VPT], T& wave_excl, T* s_wave)
-{
-    const int lane = lane_id();
-    const int wave = (int)(threadIdx.x / kWave);
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-        for (int j = 1; j < V; ++j)
-            e[k * V + j] = e[k * V + j] + e[k * V + j - 1];
-
-    T incl[VPT];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-        incl[k] = wave_inclusive_scan(e[k * V + V - 1]);
-
-    T run = T(0);
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        off[k] = run + wave_shift_right1(incl[k]);
-        run = run + readlane(incl[k], kWave - 1);
-    }
-    if (lane == 0) s_wave[wave] = run;
-    __syncthreads();
-    T agg = T(0), before = T(0);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const T v = s_wave[w];
-        if (w < wave) before = before + v;
-        agg = agg + v;
-    }
-    wave_excl = before;
-    return agg;
-}
-
 // The tile aggregate by a reduction (each lane's elements, then the wave, then
 // the four wave totals through LDS): known before any prefix is computed, so
 // the look-back scan can publish it at once. Out: wave_excl = sum of the
@@ -285,11 +246,10 @@ __device__ __forceinline__ T tile_reduce(const T (&e)[N], T& wave_excl, T* s_wav
     return agg;
 }
 
-// tile_local_scan and fold_wave_offsets in one pass over the vectors, within
-// the wave only: each vector's wave scan is folded into its elements as soon
-// as it is known, so only the data and a few temporaries are live (the
-// separate form keeps every vector's scan and offset live at once). Out: e =
-// each element's inclusive or exclusive sum within its wave's segment.
+// The scan within the wave, one vector at a time: each vector's serial scan,
+// then a wave scan of the vector totals folded into its elements at once, so
+// only the data and a few temporaries are live. Out: e = each element's
+// inclusive or exclusive sum within its wave's segment.
 template <typename T, int V, int VPT, bool INCLUSIVE>
 __device__ __forceinline__ void scan_in_wave(T (&e)[V * VPT])
 {
@@ -315,24 +275,40 @@ __device__ __forceinline__ void scan_in_wave(T (&e)[V * VPT])
     }
 }
 
-// Folds the per-vector offsets into the values: e becomes each element's
-// inclusive or exclusive sum within its wave's segment, and `off` is no
-// longer needed (so it holds no registers while the tile waits for its
-// prefix).
-template <typename T, int V, int VPT, bool INCLUSIVE>
-__device__ __forceinline__ void fold_wave_offsets(T (&e)[V * VPT], const T (&off)[VPT])
+// scan_in_wave, `head` added and each vector stored as soon as its values
+// are final (head: the tile's prefix plus the sums of the waves before this
+// one, so every value is final once its vector is scanned). The same empty
+// asm as in add_store_vec keeps each store ahead of the next vector's scan.
+template <typename T, int V, int VPT, bool INCLUSIVE, bool A16 = true>
+__device__ __forceinline__ void scan_store_vec(T* __restrict__ out, int64_t seg, int lane, T (&e)[V * VPT], T head)
 {
+    using Vec = typename VecOf<A16>::type;
+    Vec* p = reinterpret_cast<Vec*>(out + seg) + lane;
+    T run = head;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
+#pragma unroll
+        for (int j = 1; j < V; ++j)
+            e[k * V + j] = e[k * V + j] + e[k * V + j - 1];
+        const T incl = wave_inclusive_scan(e[k * V + V - 1]);
+        const T off = run + wave_shift_right1(incl);
+        run = run + readlane(incl, kWave - 1);
         if constexpr (INCLUSIVE) {
 #pragma unroll
             for (int j = 0; j < V; ++j)
-                e[k * V + j] = off[k] + e[k * V + j];
+                e[k * V + j] = off + e[k * V + j];
         } else {
 #pragma unroll
             for (int j = V - 1; j > 0; --j)
-                e[k * V + j] = off[k] + e[k * V + j - 1];
-            e[k * V] = off[k];
+                e[k * V + j] = off + e[k * V + j - 1];
+            e[k * V] = off;
+        }
+        Vec r;
+        __builtin_memcpy(&r, &e[k * V], kVecBytes);
+        __builtin_nontemporal_store(r, p + k * kWave);
+        if (k + 1 < VPT) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) asm volatile("" : "+v"(e[(k + 1) * V + j])::"memory");
         }
     }
 }
@@ -345,14 +321,6 @@ __device__ __forceinline__ void add_uniform(T (&e)[N], T head)
 #pragma unroll
     for (int i = 0; i < N; ++i)
         e[i] = head + e[i];
-}
-
-// Final values from the local scan and the tile's exclusive prefix.
-template <typename T, int V, int VPT, bool INCLUSIVE>
-__device__ __forceinline__ void tile_finish(T (&e)[V * VPT], const T (&off)[VPT], T wave_excl, T prefix)
-{
-    fold_wave_offsets<T, V, VPT, INCLUSIVE>(e, off);
-    add_uniform(e, prefix + wave_excl);
 }
 
 // ---------------------------------------------------------------------------
